@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of one SparSTAR attention scale on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input already
+resident in HBM: block means of Q and K, block scores, clip-aware top-k
+selection and block-sparse attention forward (five kernel launches on one
+stream).  The default workload is the 72,000-token final scale (16 heads,
+D = 128, bf16, keys = 512 text + 72,000 reference + 72,000 current, density
+0.09375).
+
+Printed: one JSON line.  `value` is selected-block attention TFLOP/s over the
+whole step (selected FLOPs / ms per scale); `ms_per_step` is ms per scale
+(score + select + attn).  `roofline` is for the attention kernel (bf16 MFMA
+peak), with its duration from HIP events recorded on the launch stream.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "selected-block attn TFLOP/s + ms per scale (score+select+attn) at 72k tokens"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_head_amd", "csrc", "attn_fwd_bf16.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def selected_flops(kv_count, kv_index, Nq, Nk, D, block=128):
+    """4*D * sum over rows of valid queries x valid keys of the kept blocks."""
+    cnt = kv_count.reshape(-1).astype(np.int64)
+    idx = kv_index.reshape(cnt.size, -1).astype(np.int64)
+    nqb = -(-Nq // block)
+    nkb = -(-Nk // block)
+    pos = np.arange(idx.shape[1])[None, :]
+    valid = (pos < cnt[:, None]) & (idx >= 0) & (idx < nkb)
+    keys = np.where(valid, np.minimum((idx + 1) * block, Nk) - idx * block, 0).sum(axis=1)
+    rows_i = np.arange(cnt.size) % nqb
+    nq = np.minimum((rows_i + 1) * block, Nq) - rows_i * block
+    return int(4 * D * (nq * keys).sum())
+
+
+def stage_bytes(w, kept):
+    """Algorithmic bytes of means(Q) + means(K) + scores + select."""
+    el = 2 if w.dtype == "bf16" else 4
+    BH = w.B * w.H
+    qk = BH * (w.Nq + w.Nk) * w.D * el
+    means = 2 * BH * (w.nqb + w.nkb) * w.D * 4
+    index = BH * w.nqb * (4 * kept + 4)
+    return qk + means + index
+
+
+def traffic_for_attention():
+    """HBM bytes per attention launch from committed rocprofv3 counter runs,
+    or None when the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(x, w, kept_F, budget_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    F = kept_F
+    t0 = time.perf_counter()
+    qd = oracle.decode(x["q"][0:1, 0:1], w.dtype)
+    kd = oracle.decode(x["k"][0:1, 0:1], w.dtype)
+    vd = oracle.decode(x["v"][0:1, 0:1], w.dtype)
+    qbar = oracle.block_means(qd)
+    kbar = oracle.block_means(kd)
+    S = oracle.block_scores(qbar, kbar)
+    cnt, idx = oracle.select_blocks(S, F, w.density)
+    t_sel = time.perf_counter() - t0
+    rows, t_att = [], 0.0
+    i = 0
+    while i < w.nqb and (t_att + t_sel < budget_s or len(rows) < 2):
+        t1 = time.perf_counter()
+        oracle.sparse_attention_rows(qd, kd, vd, cnt, idx, [(0, 0, i)])
+        t_att += time.perf_counter() - t1
+        rows.append(i)
+        i += 1
+    sub_cnt = cnt[0, 0, rows]
+    sub_idx = idx[0, 0, rows]
+    fl = 0
+    for r, ii in enumerate(rows):
+        nq = min((ii + 1) * 128, w.Nq) - ii * 128
+        ks = sum(min((j + 1) * 128, w.Nk) - j * 128 for j in sub_idx[r, :sub_cnt[r]])
+        fl += 4 * w.D * nq * ks
+    t_rows = t_att + t_sel * len(rows) / w.nqb
+    per_scale_s = (t_sel + t_att / len(rows) * w.nqb) * w.B * w.H
+    return {
+        "value": fl / t_rows / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"batch 0 head 0 of {w.B}x{w.H}: means+scores+selection for the head "
+                   f"({t_sel:.2f} s), attention for the first {len(rows)} of {w.nqb} query "
+                   f"blocks ({t_att:.2f} s); value = their selected FLOPs / (attention time + "
+                   f"their share of the head's selection time)"),
+        "ms_per_scale_extrapolated": per_scale_s * 1e3,
+        "seconds": t_sel + t_att,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="final-72k")
+    ap.add_argument("--cold", action="store_true",
+                    help="overwrite a 512 MiB buffer before every timed step (cold L2/MALL)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the SparSTAR hot path here has no multi-GPU "
+              "mode (heads would shard across GPUs with no communication).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_sparse_attention_head_amd as sp
+    from workloads import make_inputs, workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
+
+    w = workload(args.workload)
+    log(f"[bench] generating {w.name} inputs")
+    x = make_inputs(w)
+
+    def dev_t(a):
+        if w.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = dev_t(x["q"]), dev_t(x["k"]), dev_t(x["v"])
+    B, H, D = w.B, w.H, w.D
+    F = sp.forced_blocks(w.n_forced_tokens)
+    kept = sp.kept_blocks(w.nkb, F, w.density)
+    f32, i32 = torch.float32, torch.int32
+    qbar = torch.empty((B, H, w.nqb, D), dtype=f32, device=dev)
+    kbar = torch.empty((B, H, w.nkb, D), dtype=f32, device=dev)
+    S = torch.empty((B, H, w.nqb, w.nkb), dtype=f32, device=dev)
+    cnt = torch.empty((B, H, w.nqb), dtype=i32, device=dev)
+    idx = torch.empty((B, H, w.nqb, max(1, kept)), dtype=i32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, w.Nq), dtype=f32, device=dev)
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        sp.block_means(q, out=qbar)
+        if ev: ev[1].record(stream)
+        sp.block_means(k, out=kbar)
+        if ev: ev[2].record(stream)
+        sp.block_scores(qbar, kbar, out=S)
+        if ev: ev[3].record(stream)
+        sp.select_blocks(S, F, w.density, max_kept=kept, kv_count=cnt, kv_index=idx)
+        if ev: ev[4].record(stream)
+        sp.block_sparse_attn_fwd(q, k, v, cnt, idx, out=o, lse=lse)
+        if ev: ev[5].record(stream)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # pass 1: whole steps, K of them between two events
+    log(f"[bench] timing {args.steps} steps")
+    if args.cold:
+        per = []
+        for _ in range(args.steps):
+            flush.fill_(0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            b.synchronize()
+            per.append(a.elapsed_time(b))
+        ms_per_step = float(np.mean(per))
+    else:
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = a.elapsed_time(b) / args.steps
+
+    # pass 2: per-kernel durations from events on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    for e in evs:
+        if args.cold:
+            flush.fill_(0)
+        step(e)
+    torch.cuda.synchronize()
+    names = ["means_q", "means_k", "scores", "select", "attn"]
+    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                for i, n in enumerate(names)}
+
+    kv_count = cnt.cpu().numpy()
+    kv_index = idx.cpu().numpy()
+    flops = selected_flops(kv_count, kv_index, w.Nq, w.Nk, D)
+    attn_tflops = flops / (stage_ms["attn"] * 1e-3) / 1e12
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    sel_ms = sum(stage_ms[n] for n in names[:4])
+    sbytes = stage_bytes(w, kept)
+    dense_flops = 4 * D * w.Nq * w.Nk * B * H
+    traffic = traffic_for_attention()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU baseline (oracle, ~{args.cpu_budget:.0f} s)")
+        cpu = cpu_baseline(x, w, F, args.cpu_budget)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) + per-block offsets; see workloads/)",
+        "config": {**w.describe(), "kept_blocks": kept, "n_forced_blocks": F,
+                   "selected_tflop": flops / 1e12, "dense_tflop": dense_flops / 1e12,
+                   "cache": "cold" if args.cold else "warm"},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "stages": {
+            **{f"{n}_us": round(stage_ms[n] * 1e3, 2) for n in names},
+            "attn_tflops": round(attn_tflops, 2),
+            "selection_us": round(sel_ms * 1e3, 2),
+            "selection_alg_bytes": sbytes,
+            "selection_gbps": round(sbytes / (sel_ms * 1e-3) / 1e9, 1),
+            "selection_frac_hbm": round(sbytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "selection_share_of_scale": round(sel_ms / ms_per_step, 4),
+            "means_gbps": round(B * H * (w.Nq + w.Nk) * D * (2 if w.dtype == "bf16" else 4)
+                                / ((stage_ms["means_q"] + stage_ms["means_k"]) * 1e-3) / 1e9, 1),
+        },
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+"""ctypes binding of libsparstar.so (include/sparstar.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the path runs in the library's kernels.
+There is no fallback: if the library is missing the calls raise.
+"""
+import ctypes
+import math
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsparstar.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
+FP32, BF16 = 0, 1
+BLOCK = 128
+
+_i64, _f32, _f64, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
+_SIGNATURES = {
+    "sparstar_block_means": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
+    "sparstar_block_scores": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _vp, _vp]),
+    "sparstar_select_blocks": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _f64, _vp, _vp, _i64, _vp]),
+    "sparstar_block_sparse_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64,
+                                                      _i64, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
+    "sparstar_forced_blocks": (_i64, [_i64, _i64]),
+    "sparstar_kept_blocks": (_i64, [_i64, _i64, _f64]),
+    "sparstar_last_error": (ctypes.c_char_p, []),
+    "sparstar_version": (ctypes.c_int32, []),
+}
+
+_lib = None
+
+
+class SparstarError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+def lib():
+    """Load libsparstar.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_attention_head_amd.build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = h
+    return _lib
+
+
+def last_error() -> str:
+    return lib().sparstar_last_error().decode()
+
+
+def version() -> int:
+    return lib().sparstar_version()
+
+
+def forced_blocks(n_forced_tokens: int, block: int = BLOCK) -> int:
+    return lib().sparstar_forced_blocks(n_forced_tokens, block)
+
+
+def kept_blocks(nkb: int, n_forced_blocks: int, density: float) -> int:
+    return lib().sparstar_kept_blocks(nkb, n_forced_blocks, density)
+
+
+def _check(status):
+    if status != OK:
+        raise SparstarError(status, last_error())
+
+
+# --------------------------------------------------------------------------
+# torch-facing wrappers (device memory and stream plumbing only)
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def block_means(x, block=BLOCK, out=None, stream=None):
+    """x [B,H,N,D] bf16/fp32 -> [B,H,ceil(N/block),D] fp32."""
+    torch = _torch()
+    B, H, N, D = x.shape
+    nb = -(-N // block)
+    if out is None:
+        out = torch.empty((B, H, nb, D), dtype=torch.float32, device=x.device)
+    _check(lib().sparstar_block_means(_dev(x, "x"), _dtype_code(x), B, H, N, D, block,
+                                      _dev(out, "out"), _stream(stream)))
+    return out
+
+
+def block_scores(qbar, kbar, tau=None, out=None, stream=None):
+    """S [B,H,nqb,nkb] fp32 = tau * qbar kbar^T (tau = D^-1/2 by default)."""
+    torch = _torch()
+    B, H, nqb, D = qbar.shape
+    nkb = kbar.shape[2]
+    if tau is None:
+        tau = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=qbar.device)
+    _check(lib().sparstar_block_scores(_dev(qbar, "qbar"), _dev(kbar, "kbar"), B, H, nqb, nkb, D,
+                                       tau, _dev(out, "S"), _stream(stream)))
+    return out
+
+
+def select_blocks(S, n_forced_blocks, density, max_kept=None, kv_count=None, kv_index=None,
+                  stream=None):
+    """-> (kv_count [B,H,nqb] int32, kv_index [B,H,nqb,max_kept] int32)."""
+    torch = _torch()
+    B, H, nqb, nkb = S.shape
+    if max_kept is None:
+        max_kept = kept_blocks(nkb, n_forced_blocks, density)
+        if max_kept < 0:
+            raise SparstarError(ERR_INVALID_ARGUMENT, "invalid n_forced_blocks or density")
+    if kv_count is None:
+        kv_count = torch.empty((B, H, nqb), dtype=torch.int32, device=S.device)
+    if kv_index is None:
+        kv_index = torch.empty((B, H, nqb, max(1, max_kept)), dtype=torch.int32, device=S.device)
+    _check(lib().sparstar_select_blocks(_dev(S, "S"), B, H, nqb, nkb, n_forced_blocks, density,
+                                        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
+                                        max_kept, _stream(stream)))
+    return kv_count, kv_index
+
+
+def block_sparse_attn_fwd(q, k, v, kv_count, kv_index, scale=None, block=BLOCK, out=None,
+                          lse=None, return_lse=True, stream=None):
+    """O [B,H,Nq,D] (dtype of q) and LSE [B,H,Nq] fp32 over the listed key blocks."""
+    torch = _torch()
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    max_kept = kv_index.shape[-1]
+    _check(lib().sparstar_block_sparse_attn_fwd(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), B, H, Nq, Nk, D, block,
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept, scale,
+        _dev(out, "o"), _dev(lse, "lse") if lse is not None else None, _stream(stream)))
+    return out, lse
+
+
+def sparse_attention(q, k, v, n_forced_tokens, density, block=BLOCK, return_all=False,
+                     stream=None):
+    """The whole path for one scale: means -> scores -> selection -> attention."""
+    qbar = block_means(q, block, stream=stream)
+    kbar = block_means(k, block, stream=stream)
+    S = block_scores(qbar, kbar, stream=stream)
+    F = forced_blocks(n_forced_tokens, block)
+    kv_count, kv_index = select_blocks(S, F, density, stream=stream)
+    o, lse = block_sparse_attn_fwd(q, k, v, kv_count, kv_index, block=block, stream=stream)
+    if return_all:
+        return {"qbar": qbar, "kbar": kbar, "S": S, "kv_count": kv_count,
+                "kv_index": kv_index, "o": o, "lse": lse}
+    return o

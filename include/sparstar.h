@@ -1,0 +1,148 @@
+/*
+ * sparstar.h -- C ABI of the SparSTAR selected-block attention hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources: the review "Pith review of SparSTAR: Sparse
+ * Attention for SpaceTime AutoRegressive Video Synthesis", pith.science, and
+ * the SparSTAR abstract on mlsanity.com):
+ *
+ *   per (batch, head) -- "at each expensive scale and attention head"
+ *   (abstract) --
+ *     1. qbar_i, kbar_j: means of Q and K over contiguous 128-token blocks
+ *        ("What carries the argument");
+ *     2. S_ij = tau * qbar_i . kbar_j with tau = D^-1/2 (Eq. 2, same section);
+ *     3. keep the forced context blocks (text; for Clip 1 also the final
+ *        image-pyramid reference) and jointly rank every other key block
+ *        (preceding-clip reference and current scale) under the scale's
+ *        density budget ("What carries the argument", "Core claim");
+ *     4. run forward attention over the kept blocks only, from a forward
+ *        index list with no reverse index ("What carries the argument").
+ *
+ * Layout conventions (all entry points):
+ *   - Tensors are dense, row-major, head-major: Q [B,H,Nq,D], K and V
+ *     [B,H,Nk,D], O [B,H,Nq,D], means [B,H,nblocks,D], S [B,H,nqb,nkb],
+ *     kv_count [B,H,nqb], kv_index [B,H,nqb,max_kept], lse [B,H,Nq].
+ *   - Key tokens are in the order text | reference | current, so the forced
+ *     context is a prefix and is given as a number of leading key blocks.
+ *   - Every pointer is DEVICE memory owned by the caller; the library
+ *     allocates nothing and keeps no state besides a per-thread error string.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on it and returns; nothing is synchronised.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued.  A
+ * status other than SPARSTAR_OK means nothing was enqueued and no output was
+ * written; sparstar_last_error() then describes the problem.  A failed kernel
+ * launch returns SPARSTAR_ERR_HIP.
+ */
+#ifndef SPARSTAR_H_
+#define SPARSTAR_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SPARSTAR_OK = 0,
+  SPARSTAR_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad density, ... */
+  SPARSTAR_ERR_UNSUPPORTED = 2,      /* valid but not implemented (block != 128, D not 64/128) */
+  SPARSTAR_ERR_HIP = 3               /* the HIP runtime refused a launch */
+} sparstar_status;
+
+typedef enum {
+  SPARSTAR_FP32 = 0, /* IEEE float32 */
+  SPARSTAR_BF16 = 1  /* bfloat16 bit patterns (uint16) */
+} sparstar_dtype;
+
+/* Block size the library supports: the review's "Block size b = 128 tokens"
+ * ("Assumptions & free parameters"). */
+#define SPARSTAR_BLOCK 128
+
+/*
+ * Block means ("What carries the argument": block-averaged query and key
+ * vectors over contiguous 128-token blocks).
+ *   x    [B,H,N,D] of `dtype`.
+ *   out  [B,H,ceil(N/block),D] float32.  out[b,h,i,:] is the mean of tokens
+ *        [i*block, min((i+1)*block, N)); a partial last block is divided by
+ *        its own token count.  Sums are accumulated exactly enough that the
+ *        result is the fp32 rounding of the exact mean up to ~1 ulp.
+ * Requires block == 128, D in {64,128}, N >= 1.
+ */
+sparstar_status sparstar_block_means(const void* x, sparstar_dtype dtype, int64_t B, int64_t H,
+                                     int64_t N, int64_t D, int64_t block, float* out,
+                                     void* stream);
+
+/*
+ * Aggregated block scores, Eq. 2 ("What carries the argument"):
+ *   S[b,h,i,j] = tau * sum_d qbar[b,h,i,d] * kbar[b,h,j,d]
+ * qbar [B,H,nqb,D] and kbar [B,H,nkb,D] float32; S [B,H,nqb,nkb] float32.
+ * Products and sums are formed in float64 and rounded once to float32, so S
+ * is the correctly rounded score of the given means up to the fp64 sum's
+ * error.  Pass tau = 1/sqrt(D) for the method's score.
+ * Requires D in {64,128}, nqb >= 1, nkb >= 1.
+ */
+sparstar_status sparstar_block_scores(const float* qbar, const float* kbar, int64_t B, int64_t H,
+                                      int64_t nqb, int64_t nkb, int64_t D, float tau, float* S,
+                                      void* stream);
+
+/*
+ * Clip-aware joint Top-K ("What carries the argument", "Core claim").
+ * For every row (b,h,i) of S [B,H,nqb,nkb]:
+ *   - blocks [0, n_forced_blocks) are always kept (text, and for Clip 1 the
+ *     image-pyramid reference);
+ *   - of the E = nkb - n_forced_blocks eligible blocks, the
+ *     k = ceil(density * E) with the largest S are kept (density * E is one
+ *     rounded double product); equal scores go to the lower block index;
+ *     NaN ranks below every number, -0.0 equals +0.0;
+ *   - kv_count[b,h,i] = n_forced_blocks + k;
+ *   - kv_index[b,h,i,:] lists the kept blocks in ascending order, then -1
+ *     up to max_kept.
+ * Requires 0 <= n_forced_blocks <= nkb, 0 <= density <= 1 and
+ * max_kept >= sparstar_kept_blocks(nkb, n_forced_blocks, density).
+ * The output is the forward index only; no reverse (key -> query) index is
+ * built, matching the forward-only path the review describes.
+ */
+sparstar_status sparstar_select_blocks(const float* S, int64_t B, int64_t H, int64_t nqb,
+                                       int64_t nkb, int64_t n_forced_blocks, double density,
+                                       int32_t* kv_count, int32_t* kv_index, int64_t max_kept,
+                                       void* stream);
+
+/*
+ * Block-sparse forward attention ("What carries the argument": the chosen
+ * blocks are executed through a forward-only path).
+ * For every query token t of query block i of (b,h):
+ *   O[b,h,t,:] = sum_s softmax_s(scale * q_t . k_s) * v_s
+ *   lse[b,h,t] = log sum_s exp(scale * q_t . k_s)
+ * where s runs over the valid keys (s < Nk) of the blocks
+ * kv_index[b,h,i,0 .. kv_count[b,h,i]-1].  No causal mask is applied.
+ * Index entries outside [0, ceil(Nk/block)) are skipped; kv_count is clamped
+ * to [0, max_kept].  A row with no valid block gives O = 0 and lse = -inf.
+ *   q [B,H,Nq,D], k, v [B,H,Nk,D] of `dtype`; o [B,H,Nq,D] of `dtype`;
+ *   lse [B,H,Nq] float32, may be NULL.
+ * bf16 inputs run on bf16 MFMA with float32 accumulation and a float32
+ * online softmax; float32 inputs run in float32 throughout.
+ * Requires block == 128, D in {64,128}.
+ */
+sparstar_status sparstar_block_sparse_attn_fwd(const void* q, const void* k, const void* v,
+                                               sparstar_dtype dtype, int64_t B, int64_t H,
+                                               int64_t Nq, int64_t Nk, int64_t D, int64_t block,
+                                               const int32_t* kv_count, const int32_t* kv_index,
+                                               int64_t max_kept, float scale, void* o, float* lse,
+                                               void* stream);
+
+/* Host-only helpers (no HIP call, no error state). */
+/* ceil(n_forced_tokens / block): leading blocks that hold forced tokens; -1 on bad input. */
+int64_t sparstar_forced_blocks(int64_t n_forced_tokens, int64_t block);
+/* n_forced_blocks + ceil(density * (nkb - n_forced_blocks)); -1 on bad input. */
+int64_t sparstar_kept_blocks(int64_t nkb, int64_t n_forced_blocks, double density);
+/* Message of the last failed call on this thread ("" if none). */
+const char* sparstar_last_error(void);
+/* Library ABI version (major * 10000 + minor * 100 + patch). */
+int32_t sparstar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSTAR_H_ */

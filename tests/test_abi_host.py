@@ -1,0 +1,149 @@
+"""The C ABI library: it loads, exports what include/sparstar.h declares, and its
+host-side logic (helpers, argument checks) behaves as documented.  No call here
+reaches the GPU: every compute call below fails validation first."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import block_sparse_attention_head_amd as sp
+from block_sparse_attention_head_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparstar.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparstar_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(binding._SIGNATURES), names
+    h = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(h, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (sparstar_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_version_and_helpers():
+    assert sp.version() == 10000
+    assert sp.forced_blocks(0) == 0
+    assert sp.forced_blocks(1) == 1
+    assert sp.forced_blocks(128) == 1
+    assert sp.forced_blocks(129) == 2
+    assert sp.forced_blocks(512 + 3600) == 33
+    assert sp.forced_blocks(-1) == -1
+    assert sp.kept_blocks(16, 1, 0.25) == 5
+    assert sp.kept_blocks(286, 4, 0.1875) == 57
+    assert sp.kept_blocks(1129, 4, 0.09375) == 110
+    assert sp.kept_blocks(595, 33, 0.09375) == 86
+    assert sp.kept_blocks(129, 4, 0.625) == 83
+    assert sp.kept_blocks(504, 4, 0.1875) == 98
+    assert sp.kept_blocks(1129, 4, 1.0) == 1129
+    assert sp.kept_blocks(10, 0, 0.0) == 0
+    assert sp.kept_blocks(10, 11, 0.5) == -1
+    assert sp.kept_blocks(10, 1, 1.5) == -1
+    assert sp.kept_blocks(10, 1, float("nan")) == -1
+
+
+def test_kept_blocks_matches_oracle_budget():
+    import oracle
+    for nkb in (1, 2, 7, 16, 129, 286, 504, 595, 1129):
+        for F in sorted(f for f in {0, 1, 4, nkb // 3, nkb} if f <= nkb):
+            for dens in (0.0, 0.09375, 0.1875, 0.625, 1.0, 0.1, 0.3, 0.7):
+                assert sp.kept_blocks(nkb, F, dens) == oracle.kept_blocks(nkb, F, dens)
+
+
+L = None
+
+
+def _lib():
+    return sp.lib()
+
+
+NULL = ctypes.c_void_p(None)
+FAKE = ctypes.c_void_p(4096)     # aligned, never dereferenced: validation fails first
+
+
+def _err(status, code, needle):
+    assert status == code, (status, sp.last_error())
+    assert needle in sp.last_error(), sp.last_error()
+
+
+def test_means_validation():
+    f = _lib().sparstar_block_means
+    _err(f(NULL, 1, 1, 1, 128, 128, 128, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(f(FAKE, 1, 1, 1, 128, 96, 128, FAKE, NULL), sp.ERR_UNSUPPORTED, "D must be")
+    _err(f(FAKE, 1, 1, 1, 128, 128, 64, FAKE, NULL), sp.ERR_UNSUPPORTED, "block")
+    _err(f(FAKE, 1, 0, 1, 128, 128, 128, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "B and H")
+    _err(f(FAKE, 1, 1, 1, 0, 128, 128, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "sequence")
+    _err(f(FAKE, 7, 1, 1, 128, 128, 128, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "dtype")
+    _err(f(ctypes.c_void_p(4098), 1, 1, 1, 128, 128, 128, FAKE, NULL), sp.ERR_INVALID_ARGUMENT,
+         "aligned")
+
+
+def test_scores_validation():
+    f = _lib().sparstar_block_scores
+    _err(f(FAKE, NULL, 1, 1, 4, 4, 128, 0.1, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(f(FAKE, FAKE, 1, 1, 0, 4, 128, 0.1, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "nqb")
+    _err(f(FAKE, FAKE, 1, 1, 4, 4, 32, 0.1, FAKE, NULL), sp.ERR_UNSUPPORTED, "D must be")
+    _err(f(FAKE, FAKE, 1, 1, 4, 4, 128, float("inf"), FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "tau")
+
+
+def test_select_validation():
+    f = _lib().sparstar_select_blocks
+    _err(f(NULL, 1, 1, 4, 16, 1, 0.25, FAKE, FAKE, 5, NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(f(FAKE, 1, 1, 4, 16, 17, 0.25, FAKE, FAKE, 5, NULL), sp.ERR_INVALID_ARGUMENT, "n_forced")
+    _err(f(FAKE, 1, 1, 4, 16, 1, 1.25, FAKE, FAKE, 5, NULL), sp.ERR_INVALID_ARGUMENT, "density")
+    _err(f(FAKE, 1, 1, 4, 16, 1, -0.1, FAKE, FAKE, 5, NULL), sp.ERR_INVALID_ARGUMENT, "density")
+    _err(f(FAKE, 1, 1, 4, 16, 1, 0.25, FAKE, FAKE, 4, NULL), sp.ERR_INVALID_ARGUMENT, "max_kept")
+
+
+def test_attn_validation():
+    f = _lib().sparstar_block_sparse_attn_fwd
+    args = [FAKE, FAKE, FAKE, 1, 1, 1, 256, 256, 128, 128, FAKE, FAKE, 2, 0.088, FAKE, NULL, NULL]
+
+    def call(**kw):
+        a = list(args)
+        pos = {"q": 0, "dtype": 3, "B": 4, "Nq": 6, "Nk": 7, "D": 8, "block": 9, "idx": 11,
+               "max_kept": 12, "scale": 13, "o": 14}
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    _err(call(q=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(o=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(idx=NULL), sp.ERR_INVALID_ARGUMENT, "kv_index")
+    _err(call(D=80), sp.ERR_UNSUPPORTED, "D must be")
+    _err(call(block=256), sp.ERR_UNSUPPORTED, "block")
+    _err(call(Nk=0), sp.ERR_INVALID_ARGUMENT, "sequence")
+    _err(call(scale=0.0), sp.ERR_INVALID_ARGUMENT, "scale")
+    _err(call(scale=float("nan")), sp.ERR_INVALID_ARGUMENT, "scale")
+    _err(call(max_kept=-1), sp.ERR_INVALID_ARGUMENT, "max_kept")
+    _err(call(dtype=5), sp.ERR_INVALID_ARGUMENT, "dtype")
+
+
+def test_error_cleared_on_next_call():
+    f = _lib().sparstar_block_means
+    f(NULL, 1, 1, 1, 128, 128, 128, FAKE, NULL)
+    assert sp.last_error() != ""
+    f(FAKE, 1, 1, 1, 128, 96, 128, FAKE, NULL)
+    assert "D must be" in sp.last_error()
+
+
+def test_product_path_does_not_import_oracle():
+    """The binding and the build script never reference the oracle."""
+    pkg = os.path.join(ROOT, "block_sparse_attention_head_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.lower(), fn

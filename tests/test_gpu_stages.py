@@ -1,0 +1,187 @@
+"""GPU parity, stage by stage, on seeded inputs that span several tiles and a
+ragged tail.  Every call goes through the C ABI (ctypes binding)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_head_amd as sp
+import oracle
+from tests.parity_util import (check_selection, compare_lse, compare_outputs, log, to_dev,
+                               to_f64)
+from workloads import bf16_bits_from_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(shape, dtype, seed, offset=0.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(shape, dtype=np.float32) + np.float32(offset)
+    return bf16_bits_from_f32(x) if dtype == "bf16" else x
+
+
+# ---------------------------------------------------------------- block means
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("N", [1, 127, 128, 1000, 1280])
+def test_block_means(dtype, D, N):
+    log(f"means dtype={dtype} D={D} N={N}")
+    x = _rand((2, 3, N, D), dtype, seed=N + D, offset=0.3)
+    g = to_f64(sp.block_means(to_dev(x, dtype)))
+    ref = oracle.block_means(oracle.decode(x, dtype))
+    assert g.shape == ref.shape
+    # fp32 rounding of a nearly exact mean: within 2 ulp of the float64 value
+    err = np.abs(g - ref)
+    assert np.all(err <= 2.0 ** -22 * np.abs(ref) + 1e-30), float((err / np.abs(ref)).max())
+
+
+# ---------------------------------------------------------------- block scores
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("nqb,nkb", [(1, 1), (16, 16), (70, 131), (141, 286)])
+def test_block_scores(D, nqb, nkb):
+    log(f"scores D={D} nqb={nqb} nkb={nkb}")
+    rng = np.random.default_rng(nqb * 1000 + nkb)
+    qb = (rng.standard_normal((2, 2, nqb, D)) * 0.3).astype(np.float32)
+    kb = (rng.standard_normal((2, 2, nkb, D)) * 0.3).astype(np.float32)
+    tau = 1.0 / math.sqrt(D)
+    g = to_f64(sp.block_scores(torch.from_numpy(qb).cuda(), torch.from_numpy(kb).cuda()))
+    ref = oracle.block_scores(qb.astype(np.float64), kb.astype(np.float64))
+    # float64 accumulation rounded once: within 1 ulp of the float32 value, plus
+    # the float32 rounding of tau (a common factor for every score)
+    err = np.abs(g - ref)
+    bound = 2.0 ** -22 * np.abs(ref) + 1e-9 * np.abs(ref).max()
+    assert np.all(err <= bound), float(err.max())
+
+
+# ---------------------------------------------------------------- selection
+SEL_CASES = [
+    # nkb, F, density, kind
+    (16, 1, 0.25, "normal"), (286, 4, 0.1875, "normal"), (1129, 4, 0.09375, "normal"),
+    (595, 33, 0.09375, "normal"), (129, 4, 0.625, "ties"), (300, 0, 0.5, "nan"),
+    (200, 10, 1.0, "normal"), (64, 0, 0.0, "normal"), (65, 65, 0.5, "normal"),
+    (2048, 4, 0.09375, "ties"), (2100, 4, 0.1, "normal"), (3000, 7, 0.3, "nan"),
+    (1, 0, 1.0, "normal"), (500, 3, 0.2, "inf"), (257, 2, 0.33, "zeros"),
+]
+
+
+@pytest.mark.parametrize("nkb,F,density,kind", SEL_CASES)
+def test_select_blocks(nkb, F, density, kind):
+    log(f"select nkb={nkb} F={F} density={density} kind={kind}")
+    rng = np.random.default_rng(nkb + F)
+    B, H, nqb = 1, 3, 37
+    S = rng.standard_normal((B, H, nqb, nkb)).astype(np.float32)
+    if kind == "ties":
+        S = (np.round(S * 4) / 4).astype(np.float32)
+    elif kind == "nan":
+        S[rng.random(S.shape) < 0.3] = np.nan
+    elif kind == "inf":
+        S[rng.random(S.shape) < 0.05] = np.inf
+        S[rng.random(S.shape) < 0.05] = -np.inf
+    elif kind == "zeros":
+        S[rng.random(S.shape) < 0.5] = 0.0
+        S[rng.random(S.shape) < 0.5] = -0.0
+    kept = sp.kept_blocks(nkb, F, density)
+    max_kept = kept + 3   # padding must be written as -1
+    cnt, idx = sp.select_blocks(torch.from_numpy(S).cuda(), F, density, max_kept=max_kept)
+    cnt, idx = cnt.cpu().numpy(), idx.cpu().numpy()
+    o_cnt, o_idx = oracle.select_blocks(S.astype(np.float64), F, density, max_kept=max_kept)
+    assert np.array_equal(cnt, o_cnt)
+    assert np.array_equal(idx, o_idx)
+
+
+# ---------------------------------------------------------------- attention
+def _attn_case(dtype, D, Nq, Nk, density, F_tokens, seed):
+    rng = np.random.default_rng(seed)
+    B, H = 1, 2
+    q = rng.standard_normal((B, H, Nq, D), dtype=np.float32)
+    k = rng.standard_normal((B, H, Nk, D), dtype=np.float32)
+    v = rng.standard_normal((B, H, Nk, D), dtype=np.float32)
+    nkb = -(-Nk // 128)
+    k += rng.standard_normal((B, H, nkb, 1, D), dtype=np.float32).repeat(128, axis=3).reshape(
+        B, H, nkb * 128, D)[:, :, :Nk] * np.float32(0.5)
+    if dtype == "bf16":
+        q, k, v = bf16_bits_from_f32(q), bf16_bits_from_f32(k), bf16_bits_from_f32(v)
+    qd, kd, vd = (oracle.decode(a, dtype) for a in (q, k, v))
+    res = oracle.run_pipeline(qd, kd, vd, F_tokens, density, attention=False)
+    return (q, k, v), (qd, kd, vd), res
+
+
+def _check_attn(dtype, q, k, v, qd, kd, vd, cnt, idx, what):
+    cnt_t = torch.from_numpy(np.ascontiguousarray(cnt, dtype=np.int32)).cuda()
+    idx_t = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
+    o, lse = sp.block_sparse_attn_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
+                                      cnt_t, idx_t)
+    # the oracle skips nothing, so hand it the valid entries only
+    nkb = -(-kd.shape[2] // 128)
+    rows = cnt.size
+    clean_cnt = np.zeros_like(cnt)
+    clean_idx = np.full_like(idx, -1)
+    flat_c, flat_i = clean_cnt.reshape(-1), clean_idx.reshape(rows, -1)
+    src_c, src_i = cnt.reshape(-1), idx.reshape(rows, -1)
+    for r in range(rows):
+        row = [j for j in src_i[r, :max(0, min(src_c[r], src_i.shape[1]))] if 0 <= j < nkb]
+        flat_c[r] = len(row)
+        flat_i[r, :len(row)] = row
+    o_ref, lse_ref = oracle.sparse_attention(qd, kd, vd, clean_cnt, clean_idx)
+    mx, rel = compare_outputs(to_f64(o), o_ref, dtype, what)
+    compare_lse(to_f64(lse), lse_ref, 1e-4 if dtype == "fp32" else 2e-3, what)
+    log(f"  {what}: max|dO|={mx:.3g} relL2={rel}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("Nq,Nk,density,F_tokens", [
+    (300, 1000, 0.5, 130), (128, 2048, 0.25, 128), (1, 129, 1.0, 0), (700, 777, 0.0, 200),
+])
+def test_attention(dtype, D, Nq, Nk, density, F_tokens):
+    log(f"attn dtype={dtype} D={D} Nq={Nq} Nk={Nk} density={density} F={F_tokens}")
+    (q, k, v), (qd, kd, vd), res = _attn_case(dtype, D, Nq, Nk, density, F_tokens, seed=Nq + Nk)
+    _check_attn(dtype, q, k, v, qd, kd, vd, res["kv_count"], res["kv_index"], "oracle index")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_attention_index_edge_cases(dtype):
+    """Empty rows, out-of-range entries (skipped), counts beyond max_kept
+    (clamped), a permuted list, and the dense list."""
+    log(f"attn edge cases dtype={dtype}")
+    Nq, Nk = 520, 1100
+    (q, k, v), (qd, kd, vd), res = _attn_case(dtype, 128, Nq, Nk, 0.5, 0, seed=11)
+    cnt, idx = res["kv_count"].copy(), res["kv_index"].copy()
+    nkb = 9
+    idx = np.concatenate([idx, np.full(idx.shape[:-1] + (nkb + 1 - idx.shape[-1],), -1, np.int32)],
+                         axis=-1)
+    cnt[0, 0, 0] = 0                                  # empty row -> O = 0, LSE = -inf
+    idx[0, 0, 1, 1] = nkb + 5                         # out of range -> skipped
+    idx[0, 0, 2, 0] = -7                              # negative -> skipped
+    cnt[0, 1, 0] = idx.shape[-1] + 10                 # clamped to max_kept
+    idx[0, 1, 0, :] = -1
+    idx[0, 1, 0, :3] = [8, 0, 4]                      # permuted order, includes partial block
+    idx[0, 1, 1, :nkb] = np.arange(nkb)[::-1]         # dense, reversed
+    cnt[0, 1, 1] = nkb
+    _check_attn(dtype, q, k, v, qd, kd, vd, cnt, idx, "edge cases")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_attention_order_invariance(dtype):
+    """Permuting each index list changes only the summation order."""
+    log(f"attn order invariance dtype={dtype}")
+    (q, k, v), (qd, kd, vd), res = _attn_case(dtype, 128, 640, 1500, 0.4, 256, seed=5)
+    cnt, idx = res["kv_count"], res["kv_index"].copy()
+    rng = np.random.default_rng(0)
+    for r in np.ndindex(cnt.shape):
+        c = cnt[r]
+        idx[r][:c] = rng.permutation(idx[r][:c])
+    _check_attn(dtype, q, k, v, qd, kd, vd, cnt, idx, "permuted")
+
+
+def test_selection_feeds_attention_dense_equivalence():
+    """At density 1 the GPU path equals dense softmax attention."""
+    log("dense equivalence through the whole GPU path")
+    (q, k, v), (qd, kd, vd), _ = _attn_case("bf16", 128, 384, 900, 1.0, 0, seed=3)
+    out = sp.sparse_attention(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), 0, 1.0,
+                              return_all=True)
+    assert np.all(out["kv_count"].cpu().numpy() == 8)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qd), torch.from_numpy(kd), torch.from_numpy(vd)).numpy()
+    compare_outputs(to_f64(out["o"]), ref, "bf16", "dense")
