@@ -107,8 +107,8 @@ def cpu_baseline(x, w, kept_F, budget_s):
     fl = 0
     for r, ii in enumerate(rows):
         nq = min((ii + 1) * 128, w.Nq) - ii * 128
-        ks = sum(min((j + 1) * 128, w.Nk) - j * 128 for j in sub_idx[r, :sub_cnt[r]])
-        fl += 4 * w.D * nq * ks
+        ks = sum(min((int(j) + 1) * 128, w.Nk) - int(j) * 128 for j in sub_idx[r, :sub_cnt[r]])
+        fl += 4 * int(w.D) * int(nq) * int(ks)
     t_rows = t_att + t_sel * len(rows) / w.nqb
     per_scale_s = (t_sel + t_att / len(rows) * w.nqb) * w.B * w.H
     return {
