@@ -55,7 +55,8 @@ def build(verbose: bool = False, jobs: int = 6) -> str:
         with ThreadPoolExecutor(max_workers=jobs) as ex:
             objs = list(ex.map(one, SOURCES))
         out_tmp = LIB + ".tmp"
-        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out_tmp, *objs]
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", out_tmp,
+               *objs]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")

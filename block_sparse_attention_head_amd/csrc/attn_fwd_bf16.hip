@@ -6,28 +6,41 @@
 //
 // Design (gfx950, wave64):
 //  * One workgroup per (b*h, query block) = 128 queries, 4 waves x 32
-//    queries.  Every row keeps the same number of blocks, so the grid is
-//    evenly loaded; workgroups are numbered head-major so the ones resident
-//    together walk the same head's K/V (which then stays in L2 / MALL).
-//  * Key tiles of 64 tokens (half a selected block) go through LDS, double
-//    buffered.  The next tile is fetched with gfx950's direct-to-LDS loads
-//    (global_load_lds_dwordx4: no staging registers) while the current one is
-//    computed; one barrier per tile.  LDS rows are unpadded and their 16-byte
-//    chunks XOR-swizzled per row, which keeps both LDS read patterns below
-//    free of bank conflicts.
+//    queries; two workgroups per CU (two waves per SIMD), so one wave's
+//    matrix work overlaps the other's vector work.  Every row keeps the same
+//    number of blocks, so the grid is evenly loaded.
+//  * Grid order: all XCDs work on the same head at a time (its K/V then
+//    stays in the MALL), and each XCD takes a contiguous run of that head's
+//    query blocks (neighbouring query blocks, which tend to select the same
+//    key blocks, then share the XCD's L2).
+//  * Each query block streams its selected K/V through a ring of NBUF LDS
+//    slots of kBK keys, filled by gfx950's direct-to-LDS buffer loads
+//    (buffer_load_dwordx4 ... lds: no staging registers, the tile offset in a
+//    scalar, constant per-lane offsets) NBUF-1 tiles ahead of use; one
+//    barrier per tile.  The kernel is limited by this stream (every query
+//    block reads 64 KiB per kept block), so the ring is sized to keep as
+//    many bytes in flight as LDS allows.  LDS rows are unpadded and their
+//    16-byte chunks XOR-swizzled per row, which keeps both LDS read patterns
+//    below free of bank conflicts.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in registers).
-//    The output layout then gives every lane ONE query and 16 keys of a
-//    32-key tile, so the running max / sum / rescale of the online softmax
-//    are per-lane scalars; only one exchange between lane l and l^32 per
-//    tile is needed (v_permlane32_swap).
+//    The output layout gives every lane ONE query and 16 keys of a 32-key
+//    tile, so all softmax state is per-lane scalars; one exchange between
+//    lanes l and l^32 (v_permlane32_swap) completes a row max.
 //  * The output is accumulated transposed too, O^T += V^T P^T: P (bf16) is
 //    the B operand straight from the score registers (the MFMA k index is
 //    permuted to match the score layout), and V^T is read from the natural
 //    [key][d] LDS tile with ds_read_b64_tr_b16, gfx950's transposing LDS
 //    load, using the same key permutation.
-//  * Keys past Nk (partial last block) are zero-filled on load and masked to
-//    -inf before the softmax.  Index entries outside [0, nkb) are skipped.
+//  * Vector work per score is kept to one FMA, one exp2, half a bf16 pack
+//    and half a v_dot2 (the row sum is taken over the packed bf16 weights the
+//    MFMA consumes).  The reference max is set on the first tile and only
+//    moved when a tile's weights would exceed 2^16 (detected from the row
+//    sum), so the per-tile max and the output rescale are off the common
+//    path.
+//  * Keys past Nk (partial last block) are masked to -inf before the softmax
+//    (their rows are fetched from row Nk-1, so the values are finite).  Index
+//    entries outside [0, nkb) contribute nothing.
 #include <cmath>
 
 #include "common.hpp"
@@ -36,18 +49,30 @@ namespace sparstar {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;  // keys per LDS tile
+#ifndef SPARSTAR_ATTN_BK
+#define SPARSTAR_ATTN_BK 64
+#endif
+#ifndef SPARSTAR_ATTN_NBUF
+#define SPARSTAR_ATTN_NBUF 2
+#endif
 #ifndef SPARSTAR_ATTN_WAVES_PER_EU
 #define SPARSTAR_ATTN_WAVES_PER_EU 2
 #endif
-// The running max only moves when a tile's max exceeds it by more than this
-// many log2 units; until then probabilities are taken against the old max
-// (so they stay below 2^8) and the output needs no rescale.
-constexpr float kRescaleSlack = 8.f;
+#ifndef SPARSTAR_ATTN_XCD_MAP
+#define SPARSTAR_ATTN_XCD_MAP 1
+#endif
+constexpr int kBK = SPARSTAR_ATTN_BK;      // keys per LDS tile (32 or 64)
+constexpr int kNBuf = SPARSTAR_ATTN_NBUF;  // LDS ring slots per workgroup
+constexpr int kXcds = 8;                   // XCDs of an MI355X; workgroups go round-robin
+// Weights exp2(s - m_ref) may grow up to a row sum of 2^16 before the
+// reference max is moved (fp32 accumulators and bf16 weights hold that
+// range as exactly as small values).
+constexpr float kMaxRowSum = 65536.f;
+constexpr uint32_t kBufferRsrcWord3 = 0x00020000u;  // raw buffer descriptor, gfx9 family
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float partner_lane32(float x) {
   // v_permlane32_swap(x, x): lanes < 32 receive [x[l], x[l+32]], lanes >= 32
@@ -68,26 +93,64 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);                // 8 chunks, 2 rows per 256 B
 }
 
+// s_waitcnt vmcnt(n') with the largest supported n' <= n (immediate operand;
+// waiting for more transfers than needed is always safe).
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  if (n >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, int Nq, int Nk, int nqb,
+    const uint16_t* __restrict__ v, int Nq, int Nk, int nqb, int BH,
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_index, int max_kept,
     float sl2, uint16_t* __restrict__ o, float* __restrict__ lse) {
+#if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist only in the device pass
   constexpr int ROWB = 2 * D;                 // bytes per token row
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int TILEB = kBK * ROWB;           // bytes per K (or V) tile
   constexpr int RPI = 1024 / ROWB;            // rows per 1 KB wave-wide DMA instruction
-  constexpr int DMA_PER_WAVE = TILEB / 1024 / (kThreads / 64);
+  constexpr int DPW = TILEB / 1024 / (kThreads / 64);  // DMAs per wave per tensor
+  constexpr int DPT = 2 * DPW;                // DMAs per wave per tile (K and V)
+  constexpr int TPB = kBlock / kBK;           // tiles per selected block
+  constexpr int KT = kBK / 32;                // 32-key score sub-tiles per tile
+  constexpr int NC = kBK / 16;                // 16-key P*V steps per tile
   constexpr int KSTEPS = D / 16;              // MFMA k-steps over d for S^T
   constexpr int DT = D / 32;                  // 32-row d tiles of O^T
-  __shared__ __attribute__((aligned(1024))) char lds[2][2][TILEB];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(1024))) char lds[kNBuf][2][TILEB];  // [slot][K, V]
 
-  const int64_t row = blockIdx.x;             // (bh, i), head-major
-  const int64_t bh = row / nqb;
-  const int i = static_cast<int>(row - bh * nqb);
+  // ---- which (b*h, query block) this workgroup owns -----------------------------
+  int64_t bh;
+  int i;
+  {
+    const int p = blockIdx.x;
+#if SPARSTAR_ATTN_XCD_MAP
+    // Launch p runs on XCD p % 8.  Per head the query blocks are cut into 8
+    // contiguous runs of `run` blocks, run x going to XCD x; consecutive
+    // launches still sweep one head after another.
+    const int run = (nqb + kXcds - 1) / kXcds;
+    const int per_head = run * kXcds;
+    const int head = p / per_head;
+    const int r = p - head * per_head;
+    i = (r % kXcds) * run + r / kXcds;
+    bh = head;
+    if (i >= nqb || head >= BH) return;   // padding launches (whole workgroup)
+#else
+    bh = p / nqb;
+    i = p - static_cast<int>(bh) * nqb;
+#endif
+  }
+  const int64_t row = bh * nqb + i;
   const int tid = threadIdx.x;
-  const int w = tid / 64, l = tid % 64, h = l / 32, n = l % 32;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);  // wave index (uniform)
+  const int l = tid % 64, h = l / 32, n = l % 32;
   const int g = l / 16, L = l % 16;
   const int nkb = (Nk + kBlock - 1) / kBlock;
   const int tok = i * kBlock + 32 * w + n;
@@ -109,46 +172,71 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;   // reference max (log2 units) and row sum
 
   int count = kv_count[row];
   count = count < 0 ? 0 : (count > max_kept ? max_kept : count);
   const int32_t* list = kv_index + row * static_cast<int64_t>(max_kept);
-  const uint16_t* kh = k + bh * static_cast<int64_t>(Nk) * D;
-  const uint16_t* vh = v + bh * static_cast<int64_t>(Nk) * D;
-  const int ntiles = 2 * count;
+  const uint32_t head_bytes = static_cast<uint32_t>(Nk) * ROWB;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(k + bh * static_cast<int64_t>(Nk) * D), 0, head_bytes, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(v + bh * static_cast<int64_t>(Nk) * D), 0, head_bytes, kBufferRsrcWord3);
+  const int T = TPB * count;
 
-  // valid keys in tile t (0 if its block index is out of range)
+  // Tile t = part (t % TPB) of block list[t / TPB]: first key and valid key
+  // count (0 when the index is out of range).
   auto tile_keys = [&](int t, int& key0) -> int {
-    const int j = list[t >> 1];
-    key0 = j * kBlock + (t & 1) * kBK;
+    const int j = list[t / TPB];
+    key0 = j * kBlock + (t % TPB) * kBK;
     if (j < 0 || j >= nkb) return 0;
     return min(kBK, Nk - key0);
   };
 
-  // Direct-to-LDS fetch of tile t into buffer buf.  Wave w's m-th DMA fills
-  // 1 KB of LDS = rows [RPI*u, RPI*u + RPI), u = 4*m + w; lane i lands in
-  // LDS slot i % CPR of row RPI*u + i / CPR and so fetches global chunk
-  // (slot ^ swizzle(row)).  Rows past Nk re-read row Nk-1: finite values
-  // whose scores are masked to -inf below.
-  auto fetch_tile = [&](int t, int buf) {
+  // DMA geometry: wave w's m-th transfer fills 1 KB = LDS rows [RPI*u, RPI*u + RPI),
+  // u = 4*m + w; lane l lands in slot l % CPR of row RPI*u + l / CPR and so
+  // fetches global chunk (slot ^ swizzle(row)).
+  int dma_row[DPW], dma_off[DPW];
+#pragma unroll
+  for (int m = 0; m < DPW; ++m) {
+    dma_row[m] = RPI * (4 * m + w) + l / CPR;
+    dma_off[m] = dma_row[m] * ROWB + 16 * ((l % CPR) ^ chunk_swizzle<D>(dma_row[m]));
+  }
+  // Every tile issues exactly DPT transfers per wave (the vmcnt bookkeeping
+  // below counts on it); a tile with no valid key fetches rows from the start
+  // of the sequence, which are finite and never used.
+  auto fetch_tile = [&](int t) {
     int key0;
     const int nv = tile_keys(t, key0);
-    if (nv <= 0) return;
+    const int base = nv > 0 ? key0 : 0;
+    const int slot = t % kNBuf;
+    if (nv == kBK) {   // whole tile valid: scalar tile offset + constant lane offsets
 #pragma unroll
-    for (int m = 0; m < DMA_PER_WAVE; ++m) {
-      const int u = 4 * m + w;
-      const int r = RPI * u + l / CPR;
-      const int c = (l % CPR) ^ chunk_swizzle<D>(r);
-      const int64_t off = static_cast<int64_t>(min(key0 + r, Nk - 1)) * D + 8 * c;
-      __builtin_amdgcn_global_load_lds((const global_void*)(kh + off),
-                                       (lds_void*)(&lds[buf][0][1024 * u]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const global_void*)(vh + off),
-                                       (lds_void*)(&lds[buf][1][1024 * u]), 16, 0, 0);
+      for (int m = 0; m < DPW; ++m) {
+        const int u = 4 * m + w;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(&lds[slot][0][1024 * u]), 16,
+                                                 dma_off[m], key0 * ROWB, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(&lds[slot][1][1024 * u]), 16,
+                                                 dma_off[m], key0 * ROWB, 0, 0);
+      }
+    } else {           // partial tile: rows past Nk re-read row Nk-1 (finite, masked later)
+#pragma unroll
+      for (int m = 0; m < DPW; ++m) {
+        const int u = 4 * m + w;
+        const int rr = min(base + dma_row[m], Nk - 1);
+        const int off = rr * ROWB + (dma_off[m] - dma_row[m] * ROWB);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(&lds[slot][0][1024 * u]), 16,
+                                                 off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(&lds[slot][1][1024 * u]), 16,
+                                                 off, 0, 0, 0);
+      }
     }
   };
+  // DMAs this wave may still have in flight beyond tile t once tiles up to
+  // min(T-1, t+NBUF-2) have been issued.
+  auto outstanding_after = [&](int t) { return (min(T - 1, t + kNBuf - 2) - t) * DPT; };
 
-  // per-lane LDS byte offsets of the operand reads (buffer-relative)
+  // per-lane LDS byte offsets of the operand reads (slot-relative)
   int koff[KSTEPS];                 // K operand: row n, chunk 2*ks + h
   {
     const int sw = chunk_swizzle<D>(n);
@@ -165,95 +253,103 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
       voff[hi][dt] = r * ROWB + 16 * (chunk ^ chunk_swizzle<D>(r)) + 8 * (L % 2);
     }
   }
+  const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
-  if (ntiles > 0) {
-    fetch_tile(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+  for (int t = 0; t < min(T, kNBuf - 1); ++t) fetch_tile(t);
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  for (int t = 0; t < T; ++t) {
+    wait_vmcnt_le(outstanding_after(t));   // this wave's part of tile t has landed
+    __syncthreads();                       // all parts landed; slot (t-1) % NBUF is free
+    if (t + kNBuf - 1 < T) fetch_tile(t + kNBuf - 1);
     int key0;
     const int nv = tile_keys(t, key0);
-    if (t + 1 < ntiles) fetch_tile(t + 1, buf ^ 1);
+    if (nv <= 0) continue;
+    const char* Kl = lds[t % kNBuf][0];
+    const char* Vl = lds[t % kNBuf][1];
 
-    if (nv > 0) {
-      const char* Kl = lds[buf][0];
-      const char* Vl = lds[buf][1];
-      // ---- S^T = K Q^T : two 32-key sub-tiles --------------------------------
-      f32x16 sacc[2];
+    // ---- S^T = K Q^T : KT sub-tiles of 32 keys ----------------------------------
+    f32x16 sacc[KT];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        bf16x8 a[KSTEPS];
+    for (int kt = 0; kt < KT; ++kt) {
+      bf16x8 a[KSTEPS];
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-          a[ks] = *reinterpret_cast<const bf16x8*>(Kl + 32 * kt * ROWB + koff[ks]);
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        a[ks] = *reinterpret_cast<const bf16x8*>(Kl + 32 * kt * ROWB + koff[ks]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qop[ks], sacc[kt], 0, 0, 0);
-      }
-      // sacc[kt][r] = S(key 32*kt + (r%4) + 8*(r/4) + 4*h, query n)
-      if (nv < kBK) {
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qop[ks], sacc[kt], 0, 0, 0);
+    }
+    // sacc[kt][r] = S(key 32*kt + (r%4) + 8*(r/4) + 4*h, query n)
+    if (nv < kBK) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * kt + (r % 4) + 8 * (r / 4) + 4 * h >= nv) sacc[kt][r] = -INFINITY;
-      }
-      // ---- online softmax (per lane = per query) ------------------------------
+        for (int r = 0; r < 16; ++r)
+          if (32 * kt + (r % 4) + 8 * (r / 4) + 4 * h >= nv) sacc[kt][r] = -INFINITY;
+    }
+    // ---- weights against the reference max ------------------------------------
+    // pw[c][e]: bf16 pairs of the weights of keys 16c.. of this tile, in the
+    // register order the P*V MFMA consumes; the row sum is taken over exactly
+    // these bf16 values.
+    bf16x2 pw[NC][4];
+    float ls = 0.f;
+    auto weights = [&](float m_use) {
+      ls = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kt = c / 2, r = 8 * (c % 2) + 2 * e;
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sl2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r + 1], sl2, -m_use));
+          pw[c][e] = bf16x2{static_cast<__bf16>(p0), static_cast<__bf16>(p1)};
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pw[c][e], ones, ls, false);
+        }
+    };
+    const bool first = m_ref == -INFINITY;
+    if (!__ballot(first)) weights(m_ref);
+    // First tile, or a tile whose weights outgrew the reference: take the
+    // exact tile max, move the reference, rescale, recompute.
+    const float ls_pair = ls + partner_lane32(ls);
+    if (__ballot(first || !(ls_pair <= kMaxRowSum))) {
       float mx = sacc[0][0];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kt][r]);
       mx = fmaxf(mx, partner_lane32(mx));
-      const float mt = mx * sl2;  // tile max, log2 units
-      const bool grow = mt > m_run + kRescaleSlack;  // true on the first non-empty tile
-      if (__ballot(grow)) {
-        const float m_new = grow ? mt : m_run;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
-        l_run *= alpha;
+      const float m_new = fmaxf(m_ref, mx * sl2);
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 when m_ref = -inf
+      l_run *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-        m_run = m_new;
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      m_ref = m_new;
+      weights(m_ref == -INFINITY ? 0.f : m_ref);
+    }
+    l_run += ls;
+    // ---- O^T += V^T P^T -----------------------------------------------------------
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pb[2 * e] = pw[c][e][0];
+        pb[2 * e + 1] = pw[c][e][1];
       }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      float ls = 0.f;
+      const char* vbase = Vl + 16 * c * ROWB;   // keys [16c, 16c + 16)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kt][r], sl2, -m_use));
-          sacc[kt][r] = p;
-          ls += p;
-        }
-      l_run += ls;
-      // ---- O^T += V^T P^T ---------------------------------------------------
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int kt = c / 2, r0 = 8 * (c % 2);
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[kt][r0 + e]);
-        const char* vbase = Vl + 16 * c * ROWB;   // keys [16c, 16c + 16)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + voff[0][dt]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + voff[1][dt]));
-          const bf16x8 a = __builtin_bit_cast(
-              bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
-        }
+      for (int dt = 0; dt < DT; ++dt) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + voff[0][dt]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vbase + voff[1][dt]));
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
       }
     }
-
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's DMA for tile t+1 landed
-    __syncthreads();
   }
 
   // ---- epilogue: O = O^T / l, LSE ----------------------------------------------
@@ -272,8 +368,9 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
         *reinterpret_cast<bf16x4*>(op + d) = pk;
       }
     if (lse && h == 0)
-      lse[bh * Nq + tok] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+      lse[bh * Nq + tok] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
   }
+#endif
 }
 
 }  // namespace
@@ -284,13 +381,22 @@ sparstar_status launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const
                                      int64_t max_kept, float scale, uint16_t* o, float* lse,
                                      hipStream_t s) {
   const int64_t nqb = (Nq + kBlock - 1) / kBlock;
-  const dim3 grid(static_cast<uint32_t>(BH * nqb)), block(kThreads);
+#if SPARSTAR_ATTN_XCD_MAP
+  const int64_t launches = BH * ((nqb + kXcds - 1) / kXcds) * kXcds;
+#else
+  const int64_t launches = BH * nqb;
+#endif
+  if (launches > 2147483647LL) {
+    set_error("sparstar_block_sparse_attn_fwd: grid too large");
+    return SPARSTAR_ERR_INVALID_ARGUMENT;
+  }
+  const dim3 grid(static_cast<uint32_t>(launches)), block(kThreads);
   const float sl2 = scale * 1.4426950408889634f;
   if (D == 128)
-    attn_fwd_bf16_kernel<128><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb,
+    attn_fwd_bf16_kernel<128><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, (int)BH,
                                                      kv_count, kv_index, (int)max_kept, sl2, o, lse);
   else
-    attn_fwd_bf16_kernel<64><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb,
+    attn_fwd_bf16_kernel<64><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, (int)BH,
                                                     kv_count, kv_index, (int)max_kept, sl2, o, lse);
   return check_launch("sparstar_block_sparse_attn_fwd");
 }
