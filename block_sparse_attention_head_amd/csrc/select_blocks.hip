@@ -115,12 +115,23 @@ sparstar_status launch_select_blocks(const float* S, int64_t rows, int64_t nkb, 
   const dim3 grid(static_cast<uint32_t>(wgs)), block(64 * kWaves);
   const int n = (int)nkb, f = (int)n_forced, kk = (int)k, mk = (int)max_kept;
 #define SPARSTAR_SELECT(CC) select_kernel<CC><<<grid, block, 0, s>>>(S, rows, n, f, kk, kv_count, kv_index, mk)
-  if (nkb <= 64) SPARSTAR_SELECT(1);
-  else if (nkb <= 128) SPARSTAR_SELECT(2);
-  else if (nkb <= 256) SPARSTAR_SELECT(4);
-  else if (nkb <= 512) SPARSTAR_SELECT(8);
-  else if (nkb <= 1024) SPARSTAR_SELECT(16);
-  else if (nkb <= 2048) SPARSTAR_SELECT(32);
+  // keys per lane = ceil(nkb / 64), rounded up to an instantiated count
+  const int64_t c = (nkb + 63) / 64;
+  if (c <= 1) SPARSTAR_SELECT(1);
+  else if (c <= 2) SPARSTAR_SELECT(2);
+  else if (c <= 3) SPARSTAR_SELECT(3);
+  else if (c <= 4) SPARSTAR_SELECT(4);
+  else if (c <= 6) SPARSTAR_SELECT(6);
+  else if (c <= 8) SPARSTAR_SELECT(8);
+  else if (c <= 10) SPARSTAR_SELECT(10);
+  else if (c <= 12) SPARSTAR_SELECT(12);
+  else if (c <= 14) SPARSTAR_SELECT(14);
+  else if (c <= 16) SPARSTAR_SELECT(16);
+  else if (c <= 18) SPARSTAR_SELECT(18);
+  else if (c <= 20) SPARSTAR_SELECT(20);
+  else if (c <= 24) SPARSTAR_SELECT(24);
+  else if (c <= 28) SPARSTAR_SELECT(28);
+  else if (c <= 32) SPARSTAR_SELECT(32);
   else SPARSTAR_SELECT(0);
 #undef SPARSTAR_SELECT
   return check_launch("sparstar_select_blocks");
