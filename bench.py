@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 METRIC = "selected-block attn TFLOP/s + ms per scale (score+select+attn) at 72k tokens"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.txt")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_head_amd", "csrc", "attn_fwd_bf16.hip")
 
 
@@ -62,17 +62,23 @@ def stage_bytes(w, kept):
     return qk + means + index
 
 
-def traffic_for_attention():
-    """HBM bytes per attention launch from committed rocprofv3 counter runs,
-    or None when the kernel source changed since they were taken."""
+def traffic_for_attention(workload_name):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs
+    (calibrated FETCH_SIZE + WRITE_SIZE), or None when they were taken on
+    another workload or the kernel source changed since."""
     try:
+        rec = {}
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
+            for line in f:
+                if line.startswith("#") or ":" not in line:
+                    continue
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
         sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != sha:
+        if rec.get("source_sha256") != sha or rec.get("workload") != workload_name:
             return None
-        return rec.get("hbm_bytes_per_launch")
-    except (OSError, ValueError):
+        return int(float(rec["hbm_bytes_per_launch"]))
+    except (OSError, ValueError, KeyError):
         return None
 
 
@@ -246,7 +252,7 @@ def main():
     sel_ms = sum(stage_ms[n] for n in names[:4])
     sbytes = stage_bytes(w, kept)
     dense_flops = 4 * D * w.Nq * w.Nk * B * H
-    traffic = traffic_for_attention()
+    traffic = traffic_for_attention(w.name)
 
     cpu = None
     if not args.no_cpu_baseline:
