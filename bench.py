@@ -3,8 +3,8 @@
 
 A step is the whole hot path over one batch of synthetic input already
 resident in HBM: block means of Q and K, block scores, clip-aware top-k
-selection and block-sparse attention forward (five kernel launches on one
-stream).  The default workload is the 72,000-token final scale (16 heads,
+selection and block-sparse attention forward, on one stream (with --fused,
+scores and selection run as one launch and the scores stay on chip).  The default workload is the 72,000-token final scale (16 heads,
 D = 128, bf16, keys = 512 text + 72,000 reference + 72,000 current, density
 0.09375).
 
@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--fused", action="store_true",
+                    help="scores and selection in one launch (scores stay on chip) instead of two")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -184,7 +186,8 @@ def main():
     f32, i32 = torch.float32, torch.int32
     qbar = torch.empty((B, H, w.nqb, D), dtype=f32, device=dev)
     kbar = torch.empty((B, H, w.nkb, D), dtype=f32, device=dev)
-    S = torch.empty((B, H, w.nqb, w.nkb), dtype=f32, device=dev)
+    fused = args.fused and w.nkb <= sp.FUSED_MAX_NKB
+    S = None if fused else torch.empty((B, H, w.nqb, w.nkb), dtype=f32, device=dev)
     cnt = torch.empty((B, H, w.nqb), dtype=i32, device=dev)
     idx = torch.empty((B, H, w.nqb, max(1, kept)), dtype=i32, device=dev)
     o = torch.empty_like(q)
@@ -192,18 +195,27 @@ def main():
     stream = torch.cuda.current_stream()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
 
+    if fused:
+        names = ["means_q", "means_k", "scores_select", "attn"]
+        calls = [lambda: sp.block_means(q, out=qbar),
+                 lambda: sp.block_means(k, out=kbar),
+                 lambda: sp.select_blocks_from_means(qbar, kbar, F, w.density, max_kept=kept,
+                                                     kv_count=cnt, kv_index=idx),
+                 lambda: sp.block_sparse_attn_fwd(q, k, v, cnt, idx, out=o, lse=lse)]
+    else:
+        names = ["means_q", "means_k", "scores", "select", "attn"]
+        calls = [lambda: sp.block_means(q, out=qbar),
+                 lambda: sp.block_means(k, out=kbar),
+                 lambda: sp.block_scores(qbar, kbar, out=S),
+                 lambda: sp.select_blocks(S, F, w.density, max_kept=kept, kv_count=cnt,
+                                          kv_index=idx),
+                 lambda: sp.block_sparse_attn_fwd(q, k, v, cnt, idx, out=o, lse=lse)]
+
     def step(ev=None):
-        if ev: ev[0].record(stream)
-        sp.block_means(q, out=qbar)
-        if ev: ev[1].record(stream)
-        sp.block_means(k, out=kbar)
-        if ev: ev[2].record(stream)
-        sp.block_scores(qbar, kbar, out=S)
-        if ev: ev[3].record(stream)
-        sp.select_blocks(S, F, w.density, max_kept=kept, kv_count=cnt, kv_index=idx)
-        if ev: ev[4].record(stream)
-        sp.block_sparse_attn_fwd(q, k, v, cnt, idx, out=o, lse=lse)
-        if ev: ev[5].record(stream)
+        for i, c in enumerate(calls):
+            if ev: ev[i].record(stream)
+            c()
+        if ev: ev[len(calls)].record(stream)
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -234,13 +246,13 @@ def main():
         ms_per_step = a.elapsed_time(b) / args.steps
 
     # pass 2: per-kernel durations from events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(args.steps)]
     for e in evs:
         if args.cold:
             flush.fill_(0)
         step(e)
     torch.cuda.synchronize()
-    names = ["means_q", "means_k", "scores", "select", "attn"]
     stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
                 for i, n in enumerate(names)}
 
@@ -249,7 +261,7 @@ def main():
     flops = selected_flops(kv_count, kv_index, w.Nq, w.Nk, D)
     attn_tflops = flops / (stage_ms["attn"] * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
-    sel_ms = sum(stage_ms[n] for n in names[:4])
+    sel_ms = sum(stage_ms[n] for n in names[:-1])
     sbytes = stage_bytes(w, kept)
     dense_flops = 4 * D * w.Nq * w.Nk * B * H
     traffic = traffic_for_attention(w.name)
@@ -274,7 +286,8 @@ def main():
         "data": "synthetic (seeded N(0,1) + per-block offsets; see workloads/)",
         "config": {**w.describe(), "kept_blocks": kept, "n_forced_blocks": F,
                    "selected_tflop": flops / 1e12, "dense_tflop": dense_flops / 1e12,
-                   "cache": "cold" if args.cold else "warm"},
+                   "cache": "cold" if args.cold else "warm",
+                   "score_select": "fused" if fused else "two-step"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},

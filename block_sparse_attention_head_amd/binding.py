@@ -14,12 +14,15 @@ LIB_PATH = os.path.join(PKG, "libsparstar.so")
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 FP32, BF16 = 0, 1
 BLOCK = 128
+FUSED_MAX_NKB = 2048   # sparstar_select_blocks_from_means keeps a row of scores per q block in LDS
 
 _i64, _f32, _f64, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 _SIGNATURES = {
     "sparstar_block_means": (ctypes.c_int, [_vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64, _vp, _vp]),
     "sparstar_block_scores": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _vp, _vp]),
     "sparstar_select_blocks": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _f64, _vp, _vp, _i64, _vp]),
+    "sparstar_select_blocks_from_means": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _i64,
+                                                         _f64, _vp, _vp, _i64, _vp]),
     "sparstar_block_sparse_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64,
                                                       _i64, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
     "sparstar_forced_blocks": (_i64, [_i64, _i64]),
@@ -149,6 +152,29 @@ def select_blocks(S, n_forced_blocks, density, max_kept=None, kv_count=None, kv_
     return kv_count, kv_index
 
 
+def select_blocks_from_means(qbar, kbar, n_forced_blocks, density, tau=None, max_kept=None,
+                             kv_count=None, kv_index=None, stream=None):
+    """Scores and selection in one launch (S stays on chip); nkb <= FUSED_MAX_NKB."""
+    torch = _torch()
+    B, H, nqb, D = qbar.shape
+    nkb = kbar.shape[2]
+    if tau is None:
+        tau = 1.0 / math.sqrt(D)
+    if max_kept is None:
+        max_kept = kept_blocks(nkb, n_forced_blocks, density)
+        if max_kept < 0:
+            raise SparstarError(ERR_INVALID_ARGUMENT, "invalid n_forced_blocks or density")
+    if kv_count is None:
+        kv_count = torch.empty((B, H, nqb), dtype=torch.int32, device=qbar.device)
+    if kv_index is None:
+        kv_index = torch.empty((B, H, nqb, max(1, max_kept)), dtype=torch.int32,
+                               device=qbar.device)
+    _check(lib().sparstar_select_blocks_from_means(
+        _dev(qbar, "qbar"), _dev(kbar, "kbar"), B, H, nqb, nkb, D, tau, n_forced_blocks, density,
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept, _stream(stream)))
+    return kv_count, kv_index
+
+
 def block_sparse_attn_fwd(q, k, v, kv_count, kv_index, scale=None, block=BLOCK, out=None,
                           lse=None, return_lse=True, stream=None):
     """O [B,H,Nq,D] (dtype of q) and LSE [B,H,Nq] fp32 over the listed key blocks."""
@@ -170,13 +196,21 @@ def block_sparse_attn_fwd(q, k, v, kv_count, kv_index, scale=None, block=BLOCK, 
 
 
 def sparse_attention(q, k, v, n_forced_tokens, density, block=BLOCK, return_all=False,
-                     stream=None):
-    """The whole path for one scale: means -> scores -> selection -> attention."""
+                     fused=False, stream=None):
+    """The whole path for one scale: means -> scores -> selection -> attention.
+
+    With ``fused`` (and nkb <= FUSED_MAX_NKB) scores and selection run as one
+    launch and S is never materialised (``return_all`` then gives S = None).
+    """
     qbar = block_means(q, block, stream=stream)
     kbar = block_means(k, block, stream=stream)
-    S = block_scores(qbar, kbar, stream=stream)
     F = forced_blocks(n_forced_tokens, block)
-    kv_count, kv_index = select_blocks(S, F, density, stream=stream)
+    if fused and kbar.shape[2] <= FUSED_MAX_NKB:
+        S = None
+        kv_count, kv_index = select_blocks_from_means(qbar, kbar, F, density, stream=stream)
+    else:
+        S = block_scores(qbar, kbar, stream=stream)
+        kv_count, kv_index = select_blocks(S, F, density, stream=stream)
     o, lse = block_sparse_attn_fwd(q, k, v, kv_count, kv_index, block=block, stream=stream)
     if return_all:
         return {"qbar": qbar, "kbar": kbar, "S": S, "kv_count": kv_count,

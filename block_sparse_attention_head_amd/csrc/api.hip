@@ -148,6 +148,41 @@ sparstar_status sparstar_select_blocks(const float* S, int64_t B, int64_t H, int
                               kv_count, kv_index, max_kept, static_cast<hipStream_t>(stream));
 }
 
+sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float* kbar,
+                                                  int64_t B, int64_t H, int64_t nqb, int64_t nkb,
+                                                  int64_t D, float tau, int64_t n_forced_blocks,
+                                                  double density, int32_t* kv_count,
+                                                  int32_t* kv_index, int64_t max_kept,
+                                                  void* stream) {
+  const char* fn = "sparstar_select_blocks_from_means";
+  clear_error();
+  if (!qbar || !kbar || !kv_count || !kv_index) return invalid(fn, "null pointer");
+  if (!aligned16(qbar) || !aligned16(kbar)) return invalid(fn, "qbar and kbar must be 16-byte aligned");
+  if (nqb < 1 || nkb < 1) return invalid(fn, "nqb and nkb must be >= 1");
+  sparstar_status st = check_bhnd(fn, B, H, nqb > nkb ? nqb : nkb, D);
+  if (st != SPARSTAR_OK) return st;
+  if (nqb > kMaxI32 / nkb || B * H > kMaxI32 / nqb) return invalid(fn, "sizes too large");
+  if (!std::isfinite(tau)) return invalid(fn, "tau must be finite");
+  if (n_forced_blocks < 0 || n_forced_blocks > nkb)
+    return invalid(fn, "n_forced_blocks must lie in [0, nkb]");
+  if (!density_ok(density)) return invalid(fn, "density must lie in [0, 1]");
+  const int64_t kept = sparstar_kept_blocks(nkb, n_forced_blocks, density);
+  if (max_kept < kept) {
+    set_error("%s: max_kept (%lld) < kept blocks per row (%lld)", fn, (long long)max_kept,
+              (long long)kept);
+    return SPARSTAR_ERR_INVALID_ARGUMENT;
+  }
+  if (max_kept > kMaxI32) return invalid(fn, "max_kept too large");
+  if (nkb > fused_select_max_nkb()) {
+    set_error("%s: nkb > %lld is not supported (use sparstar_block_scores + "
+              "sparstar_select_blocks)", fn, (long long)fused_select_max_nkb());
+    return SPARSTAR_ERR_UNSUPPORTED;
+  }
+  return launch_scores_select(qbar, kbar, B * H, nqb, nkb, D, tau, n_forced_blocks,
+                              kept - n_forced_blocks, kv_count, kv_index, max_kept,
+                              static_cast<hipStream_t>(stream));
+}
+
 sparstar_status sparstar_block_sparse_attn_fwd(const void* q, const void* k, const void* v,
                                                sparstar_dtype dtype, int64_t B, int64_t H,
                                                int64_t Nq, int64_t Nk, int64_t D, int64_t block,

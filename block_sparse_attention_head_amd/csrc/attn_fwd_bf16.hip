@@ -69,6 +69,12 @@ constexpr int kXcds = 8;                   // XCDs of an MI355X; workgroups go r
 // range as exactly as small values).
 constexpr float kMaxRowSum = 65536.f;
 constexpr uint32_t kBufferRsrcWord3 = 0x00020000u;  // raw buffer descriptor, gfx9 family
+#ifndef SPARSTAR_ATTN_KV_CPOL
+#define SPARSTAR_ATTN_KV_CPOL 0   // cache-policy bits of the K/V tile loads
+#endif
+#ifndef SPARSTAR_ATTN_S_INTERLEAVE
+#define SPARSTAR_ATTN_S_INTERLEAVE 0
+#endif
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -215,9 +221,9 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
       for (int m = 0; m < DPW; ++m) {
         const int u = 4 * m + w;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(&lds[slot][0][1024 * u]), 16,
-                                                 dma_off[m], key0 * ROWB, 0, 0);
+                                                 dma_off[m], key0 * ROWB, 0, SPARSTAR_ATTN_KV_CPOL);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(&lds[slot][1][1024 * u]), 16,
-                                                 dma_off[m], key0 * ROWB, 0, 0);
+                                                 dma_off[m], key0 * ROWB, 0, SPARSTAR_ATTN_KV_CPOL);
       }
     } else {           // partial tile: rows past Nk re-read row Nk-1 (finite, masked later)
 #pragma unroll
@@ -226,9 +232,9 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
         const int rr = min(base + dma_row[m], Nk - 1);
         const int off = rr * ROWB + (dma_off[m] - dma_row[m] * ROWB);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(&lds[slot][0][1024 * u]), 16,
-                                                 off, 0, 0, 0);
+                                                 off, 0, 0, SPARSTAR_ATTN_KV_CPOL);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(&lds[slot][1][1024 * u]), 16,
-                                                 off, 0, 0, 0);
+                                                 off, 0, 0, SPARSTAR_ATTN_KV_CPOL);
       }
     }
   };
@@ -269,6 +275,19 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
 
     // ---- S^T = K Q^T : KT sub-tiles of 32 keys ----------------------------------
     f32x16 sacc[KT];
+#if SPARSTAR_ATTN_S_INTERLEAVE
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + 32 * kt * ROWB + koff[ks]);
+        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], sacc[kt], 0, 0, 0);
+      }
+#else
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
       bf16x8 a[KSTEPS];
@@ -281,6 +300,7 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
       for (int ks = 0; ks < KSTEPS; ++ks)
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qop[ks], sacc[kt], 0, 0, 0);
     }
+#endif
     // sacc[kt][r] = S(key 32*kt + (r%4) + 8*(r/4) + 4*h, query n)
     if (nv < kBK) {
 #pragma unroll

@@ -26,6 +26,12 @@ sparstar_status launch_block_scores(const float* qbar, const float* kbar, int64_
 sparstar_status launch_select_blocks(const float* S, int64_t rows, int64_t nkb, int64_t n_forced,
                                      int64_t k, int32_t* kv_count, int32_t* kv_index,
                                      int64_t max_kept, hipStream_t s);
+sparstar_status launch_scores_select(const float* qbar, const float* kbar, int64_t BH,
+                                     int64_t nqb, int64_t nkb, int64_t D, float tau,
+                                     int64_t n_forced, int64_t k, int32_t* kv_count,
+                                     int32_t* kv_index, int64_t max_kept, hipStream_t s);
+// Largest nkb the fused score + selection kernel takes (its score rows live in LDS).
+int64_t fused_select_max_nkb();
 sparstar_status launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      int64_t BH, int64_t Nq, int64_t Nk, int64_t D,
                                      const int32_t* kv_count, const int32_t* kv_index,

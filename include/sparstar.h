@@ -77,9 +77,9 @@ sparstar_status sparstar_block_means(const void* x, sparstar_dtype dtype, int64_
  * Aggregated block scores, Eq. 2 ("What carries the argument"):
  *   S[b,h,i,j] = tau * sum_d qbar[b,h,i,d] * kbar[b,h,j,d]
  * qbar [B,H,nqb,D] and kbar [B,H,nkb,D] float32; S [B,H,nqb,nkb] float32.
- * Products and sums are formed in float64 and rounded once to float32, so S
- * is the correctly rounded score of the given means up to the fp64 sum's
- * error.  Pass tau = 1/sqrt(D) for the method's score.
+ * Products and sums are formed in float64 and tau * sum is rounded once to
+ * float32, so nearly equal scores keep the order of a float64 reference.
+ * Pass tau = 1/sqrt(D) for the method's score.
  * Requires D in {64,128}, nqb >= 1, nkb >= 1.
  */
 sparstar_status sparstar_block_scores(const float* qbar, const float* kbar, int64_t B, int64_t H,
@@ -107,6 +107,24 @@ sparstar_status sparstar_select_blocks(const float* S, int64_t B, int64_t H, int
                                        int64_t nkb, int64_t n_forced_blocks, double density,
                                        int32_t* kv_count, int32_t* kv_index, int64_t max_kept,
                                        void* stream);
+
+/*
+ * Scores and selection in one pass: the same result as
+ * sparstar_block_scores(qbar, kbar, ..., tau, S) followed by
+ * sparstar_select_blocks(S, ...), bit for bit, without S in device memory.
+ * The score of each (i, j) is formed exactly as sparstar_block_scores forms
+ * it, so the two routes rank identically.  Arguments are those of the two
+ * calls (qbar [B,H,nqb,D], kbar [B,H,nkb,D] float32; kv_count [B,H,nqb];
+ * kv_index [B,H,nqb,max_kept]) with their requirements, and additionally
+ * nkb <= 2048 (a row of scores per query block is staged on chip); larger
+ * nkb returns SPARSTAR_ERR_UNSUPPORTED.
+ */
+sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float* kbar,
+                                                  int64_t B, int64_t H, int64_t nqb, int64_t nkb,
+                                                  int64_t D, float tau, int64_t n_forced_blocks,
+                                                  double density, int32_t* kv_count,
+                                                  int32_t* kv_index, int64_t max_kept,
+                                                  void* stream);
 
 /*
  * Block-sparse forward attention ("What carries the argument": the chosen

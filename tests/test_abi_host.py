@@ -107,6 +107,33 @@ def test_select_validation():
     _err(f(FAKE, 1, 1, 4, 16, 1, 0.25, FAKE, FAKE, 4, NULL), sp.ERR_INVALID_ARGUMENT, "max_kept")
 
 
+def test_fused_select_validation():
+    f = _lib().sparstar_select_blocks_from_means
+    ok = [FAKE, FAKE, 1, 1, 4, 16, 128, 0.088, 1, 0.25, FAKE, FAKE, 5, NULL]
+
+    def call(**kw):
+        a = list(ok)
+        pos = {"qbar": 0, "nqb": 4, "nkb": 5, "D": 6, "tau": 7, "F": 8, "density": 9,
+               "cnt": 10, "max_kept": 12}
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    _err(call(qbar=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(cnt=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(qbar=ctypes.c_void_p(4100)), sp.ERR_INVALID_ARGUMENT, "aligned")
+    _err(call(nqb=0), sp.ERR_INVALID_ARGUMENT, "nqb")
+    _err(call(D=96), sp.ERR_UNSUPPORTED, "D must be")
+    _err(call(tau=float("inf")), sp.ERR_INVALID_ARGUMENT, "tau")
+    _err(call(F=17), sp.ERR_INVALID_ARGUMENT, "n_forced")
+    _err(call(density=1.5), sp.ERR_INVALID_ARGUMENT, "density")
+    _err(call(max_kept=4), sp.ERR_INVALID_ARGUMENT, "max_kept")
+    big = sp.FUSED_MAX_NKB + 1
+    _err(call(nkb=big, max_kept=big), sp.ERR_UNSUPPORTED, "nkb")
+    # the largest supported row passes validation up to the launch (not made here)
+    assert sp.FUSED_MAX_NKB == 2048
+
+
 def test_attn_validation():
     f = _lib().sparstar_block_sparse_attn_fwd
     args = [FAKE, FAKE, FAKE, 1, 1, 1, 256, 256, 128, 128, FAKE, FAKE, 2, 0.088, FAKE, NULL, NULL]

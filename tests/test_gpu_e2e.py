@@ -42,6 +42,13 @@ def test_workload(cid, w):
     torch.cuda.synchronize()
     g_cnt = out["kv_count"].cpu().numpy()
     g_idx = out["kv_index"].cpu().numpy()
+    if w.nkb <= sp.FUSED_MAX_NKB:
+        # the one-launch route selects exactly what scores + selection select
+        F = sp.forced_blocks(w.n_forced_tokens)
+        f_cnt, f_idx = sp.select_blocks_from_means(out["qbar"], out["kbar"], F, w.density)
+        assert np.array_equal(f_cnt.cpu().numpy(), g_cnt)
+        assert np.array_equal(f_idx.cpu().numpy(), g_idx)
+        log("  fused scores + selection: identical")
     o_gpu = out["o"]
     lse_gpu = out["lse"].cpu().numpy().astype(np.float64)
     del q, k, v, out

@@ -90,6 +90,66 @@ def test_select_blocks(nkb, F, density, kind):
     assert np.array_equal(idx, o_idx)
 
 
+# ------------------------------------------------- fused scores + selection
+FUSED_CASES = [
+    # D, nqb, nkb, F, density, kind
+    (128, 1, 1, 0, 1.0, "normal"), (128, 16, 16, 1, 0.25, "normal"),
+    (128, 37, 131, 4, 0.1875, "normal"), (64, 70, 286, 4, 0.1875, "normal"),
+    (128, 17, 567, 33, 0.09375, "normal"), (64, 33, 1129, 4, 0.09375, "normal"),
+    (128, 5, 2048, 4, 0.09375, "normal"), (128, 40, 300, 0, 0.5, "ties"),
+    (64, 21, 129, 4, 0.625, "ties"), (128, 9, 200, 10, 0.0, "normal"),
+    (128, 9, 65, 65, 0.5, "normal"), (64, 3, 1000, 2, 1.0, "ties"),
+]
+
+
+def _fused_means(D, nqb, nkb, kind, seed):
+    rng = np.random.default_rng(seed)
+    qb = (rng.standard_normal((2, 2, nqb, D)) * 0.3).astype(np.float32)
+    kb = (rng.standard_normal((2, 2, nkb, D)) * 0.3).astype(np.float32)
+    if kind == "ties":
+        # few distinct small dyadic values: many scores are exactly equal
+        # (dyadic values: every score is exact, distinct sums stay far apart)
+        qb = (np.round(qb * 4) / 4).astype(np.float32)
+        kb = np.round(kb * 2).clip(-1, 1).astype(np.float32)
+        kb[:, :, 1::2] = kb[:, :, 0:nkb - 1:2]     # duplicated key blocks tie exactly
+    return qb, kb
+
+
+@pytest.mark.parametrize("D,nqb,nkb,F,density,kind", FUSED_CASES)
+def test_fused_select_matches_two_step(D, nqb, nkb, F, density, kind):
+    log(f"fused select D={D} nqb={nqb} nkb={nkb} F={F} density={density} kind={kind}")
+    qb, kb = _fused_means(D, nqb, nkb, kind, seed=nqb * 7 + nkb)
+    q_t, k_t = torch.from_numpy(qb).cuda(), torch.from_numpy(kb).cuda()
+    max_kept = sp.kept_blocks(nkb, F, density) + 2
+    c1, i1 = sp.select_blocks_from_means(q_t, k_t, F, density, max_kept=max_kept)
+    S = sp.block_scores(q_t, k_t)
+    c2, i2 = sp.select_blocks(S, F, density, max_kept=max_kept)
+    c1, i1, c2, i2 = (t.cpu().numpy() for t in (c1, i1, c2, i2))
+    # same scores, same rule: identical to the two-call route
+    assert np.array_equal(c1, c2)
+    assert np.array_equal(i1, i2)
+    # and the oracle's selection up to the near-tie rule
+    ref_S = oracle.block_scores(qb.astype(np.float64), kb.astype(np.float64))
+    swaps = check_selection(ref_S, F, density, c1, i1)
+    log(f"  {c1.size} rows, {swaps} near-tie swaps")
+    if kind == "ties":
+        # exact ties in float64 stay exact ties in float32: no swap allowed
+        assert swaps == 0
+
+
+def test_fused_select_repeated_calls_share_nothing():
+    # two launches in a row on different shapes: the second is not affected by the first
+    qb, kb = _fused_means(128, 30, 700, "normal", seed=5)
+    c_a, i_a = sp.select_blocks_from_means(torch.from_numpy(qb).cuda(), torch.from_numpy(kb).cuda(),
+                                           4, 0.1)
+    qs, ks = qb[:1, :1, :3], kb[:1, :1, :50]
+    c_b, i_b = sp.select_blocks_from_means(torch.from_numpy(np.ascontiguousarray(qs)).cuda(),
+                                           torch.from_numpy(np.ascontiguousarray(ks)).cuda(), 4, 0.1)
+    for (qq, kk, c, i) in ((qb, kb, c_a, i_a), (qs, ks, c_b, i_b)):
+        ref_S = oracle.block_scores(qq.astype(np.float64), kk.astype(np.float64))
+        check_selection(ref_S, 4, 0.1, c.cpu().numpy(), i.cpu().numpy())
+
+
 # ---------------------------------------------------------------- attention
 def _attn_case(dtype, D, Nq, Nk, density, F_tokens, seed):
     rng = np.random.default_rng(seed)
