@@ -13,13 +13,14 @@
 //    stays in the MALL), and each XCD takes a contiguous run of that head's
 //    query blocks (neighbouring query blocks, which tend to select the same
 //    key blocks, then share the XCD's L2).
-//  * Each query block streams its selected K/V through a ring of NBUF LDS
-//    slots of kBK keys, filled by gfx950's direct-to-LDS buffer loads
+//  * Each query block streams its selected K/V through a two-slot LDS ring
+//    of kBK-key tiles, filled by gfx950's direct-to-LDS buffer loads
 //    (buffer_load_dwordx4 ... lds: no staging registers, the tile offset in a
-//    scalar, constant per-lane offsets) NBUF-1 tiles ahead of use; one
-//    barrier per tile.  The kernel is limited by this stream (every query
-//    block reads 64 KiB per kept block), so the ring is sized to keep as
-//    many bytes in flight as LDS allows.  LDS rows are unpadded and their
+//    scalar, constant per-lane offsets) one tile ahead of use; one barrier
+//    per tile.  The kernel is limited by this stream (every query block
+//    reads 64 KiB per kept block), so the next tile's transfer must overlap
+//    all of the current tile's work: the slots are separate LDS variables
+//    (see below) so that no LDS read waits for it.  LDS rows are unpadded and their
 //    16-byte chunks XOR-swizzled per row, which keeps both LDS read patterns
 //    below free of bank conflicts.
 //  * Scores are computed transposed, S^T = K Q^T, with
@@ -52,9 +53,6 @@ constexpr int kThreads = 256;
 #ifndef SPARSTAR_ATTN_BK
 #define SPARSTAR_ATTN_BK 64
 #endif
-#ifndef SPARSTAR_ATTN_NBUF
-#define SPARSTAR_ATTN_NBUF 2
-#endif
 #ifndef SPARSTAR_ATTN_WAVES_PER_EU
 #define SPARSTAR_ATTN_WAVES_PER_EU 2
 #endif
@@ -62,7 +60,6 @@ constexpr int kThreads = 256;
 #define SPARSTAR_ATTN_XCD_MAP 1
 #endif
 constexpr int kBK = SPARSTAR_ATTN_BK;      // keys per LDS tile (32 or 64)
-constexpr int kNBuf = SPARSTAR_ATTN_NBUF;  // LDS ring slots per workgroup
 constexpr int kXcds = 8;                   // XCDs of an MI355X; workgroups go round-robin
 // Weights exp2(s - m_ref) may grow up to a row sum of 2^16 before the
 // reference max is moved (fp32 accumulators and bf16 weights hold that
@@ -99,19 +96,6 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);                // 8 chunks, 2 rows per 256 B
 }
 
-// s_waitcnt vmcnt(n') with the largest supported n' <= n (immediate operand;
-// waiting for more transfers than needed is always safe).
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  if (n >= 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if (n >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (n >= 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else if (n >= 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (n >= 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else if (n >= 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if (n >= 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -124,13 +108,20 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
   constexpr int TILEB = kBK * ROWB;           // bytes per K (or V) tile
   constexpr int RPI = 1024 / ROWB;            // rows per 1 KB wave-wide DMA instruction
   constexpr int DPW = TILEB / 1024 / (kThreads / 64);  // DMAs per wave per tensor
-  constexpr int DPT = 2 * DPW;                // DMAs per wave per tile (K and V)
   constexpr int TPB = kBlock / kBK;           // tiles per selected block
   constexpr int KT = kBK / 32;                // 32-key score sub-tiles per tile
   constexpr int NC = kBK / 16;                // 16-key P*V steps per tile
   constexpr int KSTEPS = D / 16;              // MFMA k-steps over d for S^T
   constexpr int DT = D / 32;                  // 32-row d tiles of O^T
-  __shared__ __attribute__((aligned(1024))) char lds[kNBuf][2][TILEB];  // [slot][K, V]
+  // Two ring slots of a K and a V tile.  Four separate variables, not one
+  // array: each then carries its own alias scope, so the compiler can see
+  // that reads of one slot do not touch the slot the DMA is filling and does
+  // not make them wait for it (with one array it waits for the in-flight
+  // tile before the V reads of every tile).
+  __shared__ __attribute__((aligned(1024))) char ldsK0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char ldsV0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char ldsK1[TILEB];
+  __shared__ __attribute__((aligned(1024))) char ldsV1[TILEB];
 
   // ---- which (b*h, query block) this workgroup owns -----------------------------
   int64_t bh;
@@ -208,21 +199,20 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
     dma_row[m] = RPI * (4 * m + w) + l / CPR;
     dma_off[m] = dma_row[m] * ROWB + 16 * ((l % CPR) ^ chunk_swizzle<D>(dma_row[m]));
   }
-  // Every tile issues exactly DPT transfers per wave (the vmcnt bookkeeping
-  // below counts on it); a tile with no valid key fetches rows from the start
-  // of the sequence, which are finite and never used.
-  auto fetch_tile = [&](int t) {
+  // Every tile issues the same 2 * DPW transfers per wave; a tile with no
+  // valid key fetches rows from the start of the sequence, which are finite
+  // and never used.
+  auto fetch_tile = [&](int t, char* kdst, char* vdst) {
     int key0;
     const int nv = tile_keys(t, key0);
     const int base = nv > 0 ? key0 : 0;
-    const int slot = t % kNBuf;
     if (nv == kBK) {   // whole tile valid: scalar tile offset + constant lane offsets
 #pragma unroll
       for (int m = 0; m < DPW; ++m) {
         const int u = 4 * m + w;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(&lds[slot][0][1024 * u]), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + 1024 * u), 16,
                                                  dma_off[m], key0 * ROWB, 0, SPARSTAR_ATTN_KV_CPOL);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(&lds[slot][1][1024 * u]), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + 1024 * u), 16,
                                                  dma_off[m], key0 * ROWB, 0, SPARSTAR_ATTN_KV_CPOL);
       }
     } else {           // partial tile: rows past Nk re-read row Nk-1 (finite, masked later)
@@ -231,16 +221,13 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
         const int u = 4 * m + w;
         const int rr = min(base + dma_row[m], Nk - 1);
         const int off = rr * ROWB + (dma_off[m] - dma_row[m] * ROWB);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(&lds[slot][0][1024 * u]), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + 1024 * u), 16,
                                                  off, 0, 0, SPARSTAR_ATTN_KV_CPOL);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(&lds[slot][1][1024 * u]), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + 1024 * u), 16,
                                                  off, 0, 0, SPARSTAR_ATTN_KV_CPOL);
       }
     }
   };
-  // DMAs this wave may still have in flight beyond tile t once tiles up to
-  // min(T-1, t+NBUF-2) have been issued.
-  auto outstanding_after = [&](int t) { return (min(T - 1, t + kNBuf - 2) - t) * DPT; };
 
   // per-lane LDS byte offsets of the operand reads (slot-relative)
   int koff[KSTEPS];                 // K operand: row n, chunk 2*ks + h
@@ -261,17 +248,19 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
   }
   const bf16x2 ones = {static_cast<__bf16>(1.f), static_cast<__bf16>(1.f)};
 
-  for (int t = 0; t < min(T, kNBuf - 1); ++t) fetch_tile(t);
-
-  for (int t = 0; t < T; ++t) {
-    wait_vmcnt_le(outstanding_after(t));   // this wave's part of tile t has landed
-    __syncthreads();                       // all parts landed; slot (t-1) % NBUF is free
-    if (t + kNBuf - 1 < T) fetch_tile(t + kNBuf - 1);
+  // One tile: wait until tile t is in slot (Kl, Vl), start the DMA of tile
+  // t + 1 into the other slot (Kn, Vn), then compute.  Called with constant
+  // slots (the loop below takes tiles in pairs) so that every LDS access
+  // names its variable.
+  auto tile_body = [&](int t, const char* Kl, const char* Vl, char* Kn, char* Vn) {
+    // Only tile t is outstanding here (tile t + 1 is issued after the
+    // barrier), so this wave waits for all its transfers.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                       // all parts landed; the other slot is free
+    if (t + 1 < T) fetch_tile(t + 1, Kn, Vn);
     int key0;
     const int nv = tile_keys(t, key0);
-    if (nv <= 0) continue;
-    const char* Kl = lds[t % kNBuf][0];
-    const char* Vl = lds[t % kNBuf][1];
+    if (nv <= 0) return;
 
     // ---- S^T = K Q^T : KT sub-tiles of 32 keys ----------------------------------
     f32x16 sacc[KT];
@@ -370,6 +359,12 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
       }
     }
+  };
+
+  if (T > 0) fetch_tile(0, ldsK0, ldsV0);
+  for (int t = 0; t < T; t += 2) {
+    tile_body(t, ldsK0, ldsV0, ldsK1, ldsV1);
+    if (t + 1 < T) tile_body(t + 1, ldsK1, ldsV1, ldsK0, ldsV0);
   }
 
   // ---- epilogue: O = O^T / l, LSE ----------------------------------------------
