@@ -69,9 +69,6 @@ constexpr uint32_t kBufferRsrcWord3 = 0x00020000u;  // raw buffer descriptor, gf
 #ifndef SPARSTAR_ATTN_KV_CPOL
 #define SPARSTAR_ATTN_KV_CPOL 0   // cache-policy bits of the K/V tile loads
 #endif
-#ifndef SPARSTAR_ATTN_S_INTERLEAVE
-#define SPARSTAR_ATTN_S_INTERLEAVE 0
-#endif
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
@@ -264,7 +261,7 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
 
     // ---- S^T = K Q^T : KT sub-tiles of 32 keys ----------------------------------
     f32x16 sacc[KT];
-#if SPARSTAR_ATTN_S_INTERLEAVE
+    // the KT accumulation chains interleave, so consecutive MFMAs are independent
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -276,20 +273,6 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + 32 * kt * ROWB + koff[ks]);
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], sacc[kt], 0, 0, 0);
       }
-#else
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      bf16x8 a[KSTEPS];
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        a[ks] = *reinterpret_cast<const bf16x8*>(Kl + 32 * kt * ROWB + koff[ks]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qop[ks], sacc[kt], 0, 0, 0);
-    }
-#endif
     // sacc[kt][r] = S(key 32*kt + (r%4) + 8*(r/4) + 4*h, query n)
     if (nv < kBK) {
 #pragma unroll
