@@ -7,5 +7,5 @@ binding) never imports, calls or links anything here.
 from .sparstar_oracle import (  # noqa: F401
     decode, block_means, block_scores, forced_blocks, budget, kept_blocks,
     select_blocks, select_row, sparse_attention, sparse_attention_rows,
-    run_pipeline, selected_flops,
+    run_pipeline, selected_flops, retained_mass_rows, token_topk_bound_rows,
 )

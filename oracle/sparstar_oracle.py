@@ -198,6 +198,69 @@ def sparse_attention(q, k, v, kv_count, kv_index, block=128, scale=None):
 
 
 # ---------------------------------------------------------------------------
+# Diagnostic -- retained attention mass and the token-wise Top-K bound
+# ([R] "Core claim": block-wise Top-K recomputed per scale is compared with a
+# token-wise upper bound by the attention mass it retains; [R] "Editorial
+# extensions": the exact token-wise Top-K oracle at the same densities)
+# ---------------------------------------------------------------------------
+def _dense_probs(q_blk, k, scale):
+    """Dense softmax rows p[t, s] of one query block over all Nk keys."""
+    logits = scale * (q_blk @ k.T)
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def retained_mass_rows(q, k, kv_count, kv_index, rows, block=128, scale=None):
+    """Retained attention mass of the kept blocks, per query token.
+
+    For query t of block i: the sum, over the valid keys of the kept blocks,
+    of t's dense softmax probabilities (softmax over all Nk keys).  1 when
+    every block is kept.  Returns {(b,h,i): mass [n]}.
+    """
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    Nq, Nk = q.shape[2], k.shape[2]
+    out = {}
+    for (b, h, i) in rows:
+        qb = q[b, h, i * block:min((i + 1) * block, Nq)]
+        p = _dense_probs(qb, k[b, h], scale)
+        c = int(kv_count[b, h, i])
+        keep = np.zeros(Nk, dtype=bool)
+        for j in kv_index[b, h, i, :c]:
+            if 0 <= j and j * block < Nk:
+                keep[j * block:min((j + 1) * block, Nk)] = True
+        out[(b, h, i)] = p[:, keep].sum(axis=1)
+    return out
+
+
+def token_topk_bound_rows(q, k, n_forced_blocks, k_blocks, rows, block=128, scale=None):
+    """Token-wise Top-K upper bound at the same budget, per query token.
+
+    The block policy keeps the forced prefix blocks and k_blocks eligible
+    blocks, i.e. at most k_blocks * block eligible tokens.  The token-wise
+    policy keeps the same forced tokens and, per query token, the
+    k_blocks * block eligible keys of largest dense probability; its retained
+    mass bounds the block policy's from above.  Returns {(b,h,i): bound [n]}.
+    """
+    D = q.shape[-1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    Nq, Nk = q.shape[2], k.shape[2]
+    f_tok = min(n_forced_blocks * block, Nk)
+    m_tok = min(k_blocks * block, Nk - f_tok)
+    out = {}
+    for (b, h, i) in rows:
+        qb = q[b, h, i * block:min((i + 1) * block, Nq)]
+        p = _dense_probs(qb, k[b, h], scale)
+        forced = p[:, :f_tok].sum(axis=1)
+        elig = np.sort(p[:, f_tok:], axis=1)[:, ::-1]
+        out[(b, h, i)] = forced + elig[:, :m_tok].sum(axis=1)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Whole path and counting helpers
 # ---------------------------------------------------------------------------
 def run_pipeline(q, k, v, n_forced_tokens, density, block=128, attention=True):

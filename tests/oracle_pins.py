@@ -270,6 +270,106 @@ def pin_selected_flops(impl):
     assert impl.selected_flops(count2, index2, 10, 9 * b + 5, D, b) == 4 * D * 10 * (b + 5)
 
 
+# --- retained attention mass and the token-wise Top-K bound -------------------
+def _textbook_probs(q, k, scale):
+    """Dense softmax probabilities, one query at a time with exact sums."""
+    out = []
+    for t in range(q.shape[0]):
+        logits = [scale * math.fsum(q[t, d] * k[s, d] for d in range(q.shape[1]))
+                  for s in range(k.shape[0])]
+        mx = max(logits)
+        w = [math.exp(x - mx) for x in logits]
+        z = math.fsum(w)
+        out.append([x / z for x in w])
+    return out
+
+
+def pin_retained_mass(impl, seed=8):
+    """Retained mass = dense softmax probability summed over the kept keys
+    ([R] 'Core claim'): brute force on tiny inputs; exactly 1 when every block
+    is kept; never decreasing as the density grows (top-k sets are nested);
+    equal to exp(LSE over kept keys - LSE over all keys)."""
+    rng = np.random.default_rng(seed)
+    B, H, Nq, Nk, D, b = 1, 1, 6, 13, 4, 4
+    q = rng.standard_normal((B, H, Nq, D)) * 2
+    k = rng.standard_normal((B, H, Nk, D))
+    v = rng.standard_normal((B, H, Nk, D))
+    res = impl.run_pipeline(q, k, v, n_forced_tokens=3, density=0.34, block=b)
+    rows = [(0, 0, i) for i in range(-(-Nq // b))]
+    got = impl.retained_mass_rows(q, k, res["kv_count"], res["kv_index"], rows, block=b)
+    scale = 1 / math.sqrt(D)
+    for (_, _, i) in rows:
+        qb = q[0, 0, i * b:min((i + 1) * b, Nq)]
+        probs = _textbook_probs(qb, k[0, 0], scale)
+        blocks = list(res["kv_index"][0, 0, i, :res["kv_count"][0, 0, i]])
+        for t, pr in enumerate(probs):
+            ref = math.fsum(pr[s] for s in range(Nk) if s // b in blocks)
+            assert abs(got[(0, 0, i)][t] - ref) <= 1e-13, (i, t)
+    # density 1 keeps everything; nesting over densities; LSE identity
+    B, H, Nq, Nk, D, b = 1, 2, 300, 700, 16, 128
+    q = rng.standard_normal((B, H, Nq, D)) * 2
+    k = rng.standard_normal((B, H, Nk, D)) + rng.standard_normal((B, H, 1, D))
+    v = rng.standard_normal((B, H, Nk, D))
+    rows = [(0, h, i) for h in range(H) for i in range(-(-Nq // b))]
+    prev = None
+    full = impl.run_pipeline(q, k, v, n_forced_tokens=0, density=1.0, block=b)
+    for dens in (0.0, 0.2, 0.4, 0.6, 1.0):
+        res = impl.run_pipeline(q, k, v, n_forced_tokens=130, density=dens, block=b)
+        m = impl.retained_mass_rows(q, k, res["kv_count"], res["kv_index"], rows, block=b)
+        cur = np.concatenate([m[r] for r in rows])
+        assert np.all(cur > 0) and np.all(cur <= 1 + 1e-12)
+        if prev is not None:
+            assert np.all(cur >= prev - 1e-12), dens
+        for (bb, h, i) in rows:
+            lo = i * b
+            hi = lo + m[(bb, h, i)].size
+            ident = np.exp(res["lse"][bb, h, lo:hi] - full["lse"][bb, h, lo:hi])
+            assert np.abs(m[(bb, h, i)] - ident).max() <= 1e-12
+        prev = cur
+    assert np.abs(prev - 1).max() <= 1e-12
+
+
+def pin_token_topk_bound(impl, seed=9):
+    """The token-wise Top-K policy at the same budget keeps the forced tokens
+    and the k * b most probable eligible keys per query ([R] 'Core claim',
+    'Editorial extensions'): brute force by ranking probabilities on tiny
+    inputs; never below the block policy's retained mass; 1 when every
+    eligible key fits the budget; the forced mass alone when the budget is 0."""
+    rng = np.random.default_rng(seed)
+    B, H, Nq, Nk, D, b = 1, 1, 5, 14, 4, 4
+    q = rng.standard_normal((B, H, Nq, D)) * 2
+    k = rng.standard_normal((B, H, Nk, D))
+    scale = 1 / math.sqrt(D)
+    F, kb = 1, 2
+    rows = [(0, 0, i) for i in range(-(-Nq // b))]
+    got = impl.token_topk_bound_rows(q, k, F, kb, rows, block=b)
+    for (_, _, i) in rows:
+        qb = q[0, 0, i * b:min((i + 1) * b, Nq)]
+        for t, pr in enumerate(_textbook_probs(qb, k[0, 0], scale)):
+            elig = sorted(pr[F * b:], reverse=True)
+            ref = math.fsum(pr[:F * b]) + math.fsum(elig[:kb * b])
+            assert abs(got[(0, 0, i)][t] - ref) <= 1e-13, (i, t)
+    B, H, Nq, Nk, D, b = 1, 2, 300, 700, 16, 128
+    q = rng.standard_normal((B, H, Nq, D)) * 2
+    k = rng.standard_normal((B, H, Nk, D)) + rng.standard_normal((B, H, 1, D))
+    v = rng.standard_normal((B, H, Nk, D))
+    rows = [(0, h, i) for h in range(H) for i in range(-(-Nq // b))]
+    for dens in (0.0, 0.25, 0.5):
+        res = impl.run_pipeline(q, k, v, n_forced_tokens=130, density=dens, block=b, attention=False)
+        F = res["n_forced"]
+        kblk = int(res["kv_count"][0, 0, 0]) - F
+        m = impl.retained_mass_rows(q, k, res["kv_count"], res["kv_index"], rows, block=b)
+        u = impl.token_topk_bound_rows(q, k, F, kblk, rows, block=b)
+        for r in rows:
+            assert np.all(u[r] >= m[r] - 1e-12), (dens, r)
+            if kblk == 0:
+                assert np.abs(u[r] - m[r]).max() <= 1e-12
+    nkb = -(-700 // 128)
+    u = impl.token_topk_bound_rows(q, k, 2, nkb - 2, rows, block=128)
+    assert all(np.abs(u[r] - 1).max() <= 1e-12 for r in rows)
+
+
 ALL_PINS = [pin_identity, pin_means_closed_form, pin_selection_bruteforce,
             pin_ties_duplicated_blocks, pin_tiny_budget, pin_dense_equivalence,
-            pin_masked_sdpa, pin_convex_hull, pin_empty_selection, pin_selected_flops]
+            pin_masked_sdpa, pin_convex_hull, pin_empty_selection, pin_selected_flops,
+            pin_retained_mass, pin_token_topk_bound]

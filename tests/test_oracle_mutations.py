@@ -41,6 +41,14 @@ MUTATIONS = {
     "softmax-unnormalised": ("o = (e / z) @ v[keys]", "o = e @ v[keys]"),
     "empty-row-nonzero": ("return np.zeros((n, v.shape[1])), np.full(n, -np.inf)",
                           "return np.zeros((n, v.shape[1])), np.zeros(n)"),
+    "mass-normalised-over-kept": ("return e / e.sum(axis=1, keepdims=True)",
+                                  "return e / e[:, :1].sum(axis=1, keepdims=True)"),
+    "mass-skips-last-key-of-block": ("keep[j * block:min((j + 1) * block, Nk)] = True",
+                                     "keep[j * block:min((j + 1) * block, Nk) - 1] = True"),
+    "bound-takes-least-probable": ("elig = np.sort(p[:, f_tok:], axis=1)[:, ::-1]",
+                                   "elig = np.sort(p[:, f_tok:], axis=1)"),
+    "bound-ignores-forced": ("out[(b, h, i)] = forced + elig[:, :m_tok].sum(axis=1)",
+                             "out[(b, h, i)] = elig[:, :m_tok].sum(axis=1)"),
     "flops-counts-padding": ("nk = int(np.minimum((blocks + 1) * block, Nk).sum() - (blocks * block).sum())",
                              "nk = int(blocks.size * block)"),
 }
