@@ -131,6 +131,39 @@ def cpu_baseline(x, w, kept_F, budget_s):
     }
 
 
+def mass_diagnostic(sp, torch, x, w, q, k, v, cnt, idx, F, kept, sample_blocks=4):
+    """Retained attention mass of the selection (GPU, every query), and on a
+    sample of query blocks of head 0 the oracle's mass and its token-wise
+    Top-K bound at the same budget."""
+    import oracle
+    mass = sp.selection_retained_mass(q, k, v, cnt, idx)
+    torch.cuda.synchronize()
+    m = mass.float().cpu().numpy().reshape(-1)
+    qd = oracle.decode(x["q"][0:1, 0:1], w.dtype)
+    kd = oracle.decode(x["k"][0:1, 0:1], w.dtype)
+    blocks = sorted({int(round(j)) for j in np.linspace(0, w.nqb - 1, sample_blocks)})
+    rows = [(0, 0, i) for i in blocks]
+    c_np, i_np = cnt[0:1, 0:1].cpu().numpy(), idx[0:1, 0:1].cpu().numpy()
+    t0 = time.perf_counter()
+    om = oracle.retained_mass_rows(qd, kd, c_np, i_np, rows)
+    ub = oracle.token_topk_bound_rows(qd, kd, F, kept - F, rows)
+    secs = time.perf_counter() - t0
+    om_all = np.concatenate([om[r] for r in rows])
+    ub_all = np.concatenate([ub[r] for r in rows])
+    gm = mass[0, 0].float().cpu().numpy()
+    g_rows = np.concatenate([gm[i * 128:i * 128 + om[(0, 0, i)].size] for (_, _, i) in rows])
+    return {
+        "retained_mass_mean": round(float(m.mean()), 5),
+        "retained_mass_p05": round(float(np.quantile(m, 0.05)), 5),
+        "retained_mass_min": round(float(m.min()), 5),
+        "sample": f"head 0, query blocks {blocks}: oracle fp64 ({secs:.1f} s)",
+        "sample_mass_gpu": round(float(g_rows.mean()), 5),
+        "sample_mass_oracle": round(float(om_all.mean()), 5),
+        "sample_token_topk_bound": round(float(ub_all.mean()), 5),
+        "sample_mass_over_bound": round(float(om_all.mean() / ub_all.mean()), 5),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +177,8 @@ def main():
                     help="seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--fused", action="store_true",
                     help="scores and selection in one launch (scores stay on chip) instead of two")
+    ap.add_argument("--no-diagnostics", action="store_true",
+                    help="skip the retained-attention-mass diagnostic (outside the timed region)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -266,6 +301,11 @@ def main():
     dense_flops = 4 * D * w.Nq * w.Nk * B * H
     traffic = traffic_for_attention(w.name)
 
+    diag = None
+    if not args.no_diagnostics:
+        log("[bench] retained-attention-mass diagnostic")
+        diag = mass_diagnostic(sp, torch, x, w, q, k, v, cnt, idx, F, kept)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU baseline (oracle, ~{args.cpu_budget:.0f} s)")
@@ -292,6 +332,7 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
+        "diagnostics": diag,
         "stages": {
             **{f"{n}_us": round(stage_ms[n] * 1e3, 2) for n in names},
             "attn_tflops": round(attn_tflops, 2),

@@ -25,6 +25,7 @@ _SIGNATURES = {
                                                          _f64, _vp, _vp, _i64, _vp]),
     "sparstar_block_sparse_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64,
                                                       _i64, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
+    "sparstar_retained_mass": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp]),
     "sparstar_forced_blocks": (_i64, [_i64, _i64]),
     "sparstar_kept_blocks": (_i64, [_i64, _i64, _f64]),
     "sparstar_last_error": (ctypes.c_char_p, []),
@@ -193,6 +194,29 @@ def block_sparse_attn_fwd(q, k, v, kv_count, kv_index, scale=None, block=BLOCK, 
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept, scale,
         _dev(out, "o"), _dev(lse, "lse") if lse is not None else None, _stream(stream)))
     return out, lse
+
+
+def retained_mass(lse_sel, lse_dense, out=None, stream=None):
+    """exp(lse_sel - lse_dense) per query token (0 where either is -inf)."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty_like(lse_sel)
+    _check(lib().sparstar_retained_mass(_dev(lse_sel, "lse_sel"), _dev(lse_dense, "lse_dense"),
+                                        lse_sel.numel(), _dev(out, "mass"), _stream(stream)))
+    return out
+
+
+def selection_retained_mass(q, k, v, kv_count, kv_index, block=BLOCK, stream=None):
+    """Retained attention mass of a selection, per query token [B,H,Nq]: the
+    attention LSE over the listed blocks against the LSE over every block
+    (listed by the selector at n_forced_blocks = 0, density = 1)."""
+    _, lse_sel = block_sparse_attn_fwd(q, k, v, kv_count, kv_index, block=block, stream=stream)
+    qbar = block_means(q, block, stream=stream)
+    kbar = block_means(k, block, stream=stream)
+    S = block_scores(qbar, kbar, stream=stream)
+    d_cnt, d_idx = select_blocks(S, 0, 1.0, stream=stream)
+    _, lse_dense = block_sparse_attn_fwd(q, k, v, d_cnt, d_idx, block=block, stream=stream)
+    return retained_mass(lse_sel, lse_dense, stream=stream)
 
 
 def sparse_attention(q, k, v, n_forced_tokens, density, block=BLOCK, return_all=False,

@@ -183,6 +183,16 @@ sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float
                               static_cast<hipStream_t>(stream));
 }
 
+sparstar_status sparstar_retained_mass(const float* lse_sel, const float* lse_dense, int64_t n,
+                                      float* mass, void* stream) {
+  const char* fn = "sparstar_retained_mass";
+  clear_error();
+  if (n < 0) return invalid(fn, "n must be >= 0");
+  if (n == 0) return SPARSTAR_OK;
+  if (!lse_sel || !lse_dense || !mass) return invalid(fn, "null pointer");
+  return launch_retained_mass(lse_sel, lse_dense, n, mass, static_cast<hipStream_t>(stream));
+}
+
 sparstar_status sparstar_block_sparse_attn_fwd(const void* q, const void* k, const void* v,
                                                sparstar_dtype dtype, int64_t B, int64_t H,
                                                int64_t Nq, int64_t Nk, int64_t D, int64_t block,

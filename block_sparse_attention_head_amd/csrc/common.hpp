@@ -42,6 +42,9 @@ sparstar_status launch_attn_fwd_f32(const float* q, const float* k, const float*
                                     const int32_t* kv_index, int64_t max_kept, float scale,
                                     float* o, float* lse, hipStream_t s);
 
+sparstar_status launch_retained_mass(const float* lse_sel, const float* lse_dense, int64_t n,
+                                     float* mass, hipStream_t s);
+
 sparstar_status check_launch(const char* what);
 
 // ---------------------------------------------------------------------------

@@ -149,6 +149,21 @@ sparstar_status sparstar_block_sparse_attn_fwd(const void* q, const void* k, con
                                                int64_t max_kept, float scale, void* o, float* lse,
                                                void* stream);
 
+/*
+ * Retained attention mass, a diagnostic of a selection (review, "Core
+ * claim": fresh block-wise Top-K is judged by the share of dense attention
+ * mass it keeps).  For each of the n query tokens:
+ *   mass[t] = exp(lse_sel[t] - lse_dense[t])
+ * = the dense softmax probability of query t summed over the kept keys, where
+ * lse_sel comes from sparstar_block_sparse_attn_fwd with the selection and
+ * lse_dense from the same call with every block listed (e.g. the lists of
+ * sparstar_select_blocks with n_forced_blocks = 0 and density = 1).  A query
+ * with lse_sel or lse_dense equal to -inf gets 0.  All three arrays are
+ * float32 device memory of n elements; n = 0 is a no-op.
+ */
+sparstar_status sparstar_retained_mass(const float* lse_sel, const float* lse_dense, int64_t n,
+                                       float* mass, void* stream);
+
 /* Host-only helpers (no HIP call, no error state). */
 /* ceil(n_forced_tokens / block): leading blocks that hold forced tokens; -1 on bad input. */
 int64_t sparstar_forced_blocks(int64_t n_forced_tokens, int64_t block);

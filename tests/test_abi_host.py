@@ -134,6 +134,14 @@ def test_fused_select_validation():
     assert sp.FUSED_MAX_NKB == 2048
 
 
+def test_retained_mass_validation():
+    f = _lib().sparstar_retained_mass
+    _err(f(FAKE, FAKE, -1, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "n must be")
+    _err(f(NULL, FAKE, 10, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(f(FAKE, FAKE, 10, NULL, NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    assert f(NULL, NULL, 0, NULL, NULL) == sp.OK   # nothing to do, nothing touched
+
+
 def test_attn_validation():
     f = _lib().sparstar_block_sparse_attn_fwd
     args = [FAKE, FAKE, FAKE, 1, 1, 1, 256, 256, 128, 128, FAKE, FAKE, 2, 0.088, FAKE, NULL, NULL]

@@ -245,3 +245,44 @@ def test_selection_feeds_attention_dense_equivalence():
     ref = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(qd), torch.from_numpy(kd), torch.from_numpy(vd)).numpy()
     compare_outputs(to_f64(out["o"]), ref, "bf16", "dense")
+
+
+# ------------------------------------------------------ retained attention mass
+@pytest.mark.parametrize("dtype,D,Nq,Nk,density,F_tokens", [
+    ("fp32", 64, 700, 1500, 0.25, 128), ("bf16", 128, 1000, 2400, 0.1875, 300),
+    ("bf16", 64, 513, 1100, 0.5, 0),
+])
+def test_retained_mass(dtype, D, Nq, Nk, density, F_tokens):
+    log(f"retained mass dtype={dtype} D={D} Nq={Nq} Nk={Nk} density={density}")
+    (q, k, v), (qd, kd, vd), res = _attn_case(dtype, D, Nq, Nk, density, F_tokens, seed=Nq + Nk)
+    cnt, idx = res["kv_count"], res["kv_index"]
+    g = sp.selection_retained_mass(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
+                                   torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda())
+    g = to_f64(g)
+    B, H = cnt.shape[:2]
+    rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(cnt.shape[2])]
+    ref = oracle.retained_mass_rows(qd, kd, cnt, idx, rows)
+    tol = 1e-5 if dtype == "fp32" else 5e-3   # from the LSE tolerances of the two attention calls
+    worst = 0.0
+    for (b, h, i), m in ref.items():
+        got = g[b, h, i * 128:i * 128 + m.size]
+        worst = max(worst, float(np.abs(got - m).max()))
+    log(f"  max |mass - oracle| = {worst:.3g}")
+    assert worst <= tol
+
+
+def test_retained_mass_full_selection_is_one():
+    # every block kept: both LSEs come from identical lists, so the mass is exactly 1
+    (q, k, v), _, res = _attn_case("bf16", 128, 600, 900, 1.0, 0, seed=3)
+    g = sp.selection_retained_mass(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                   torch.from_numpy(res["kv_count"]).cuda(),
+                                   torch.from_numpy(res["kv_index"]).cuda())
+    assert torch.all(g == 1.0)
+
+
+def test_retained_mass_edge_values():
+    lse_s = torch.tensor([0.0, -float("inf"), 1.5, -2.0, 3.0], device="cuda")
+    lse_d = torch.tensor([0.0, 0.0, 2.0, -float("inf"), 3.0 + math.log(4.0)], device="cuda")
+    m = sp.retained_mass(lse_s, lse_d).cpu().numpy()
+    ref = np.array([1.0, 0.0, math.exp(-0.5), 0.0, 0.25])
+    assert np.allclose(m, ref, rtol=2e-7, atol=0)
