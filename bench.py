@@ -177,6 +177,8 @@ def main():
                     help="seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--fused", action="store_true",
                     help="scores and selection in one launch (scores stay on chip) instead of two")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step recorded as one HIP graph and replayed")
     ap.add_argument("--no-diagnostics", action="store_true",
                     help="skip the retained-attention-mass diagnostic (outside the timed region)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -280,6 +282,26 @@ def main():
         torch.cuda.synchronize()
         ms_per_step = a.elapsed_time(b) / args.steps
 
+    graph_ms = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = a.elapsed_time(b) / args.steps
+
     # pass 2: per-kernel durations from events on the launch stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
            for _ in range(args.steps)]
@@ -341,6 +363,7 @@ def main():
             "selection_gbps": round(sbytes / (sel_ms * 1e-3) / 1e9, 1),
             "selection_frac_hbm": round(sbytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "selection_share_of_scale": round(sel_ms / ms_per_step, 4),
+            "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
             "means_gbps": round(B * H * (w.Nq + w.Nk) * D * (2 if w.dtype == "bf16" else 4)
                                 / ((stage_ms["means_q"] + stage_ms["means_k"]) * 1e-3) / 1e9, 1),
         },

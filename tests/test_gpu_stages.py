@@ -286,3 +286,53 @@ def test_retained_mass_edge_values():
     m = sp.retained_mass(lse_s, lse_d).cpu().numpy()
     ref = np.array([1.0, 0.0, math.exp(-0.5), 0.0, 0.25])
     assert np.allclose(m, ref, rtol=2e-7, atol=0)
+
+
+# ------------------------------------------------------------- graph capture
+def test_scale_captured_in_a_graph():
+    """The whole scale (two means, scores, selection, attention) recorded as one
+    HIP graph and replayed: every replay equals the eager result bit for bit,
+    with eager work and synchronisations between replays."""
+    (q, k, v), _, res = _attn_case("bf16", 128, 1100, 2600, 0.1875, 300, seed=11)
+    qd, kd, vd = (to_dev(a, "bf16") for a in (q, k, v))
+    B, H, Nq, D = qd.shape
+    nqb, nkb = -(-Nq // 128), -(-kd.shape[2] // 128)
+    F = sp.forced_blocks(300)
+    kept = sp.kept_blocks(nkb, F, 0.1875)
+    f32, i32, dev = torch.float32, torch.int32, qd.device
+    bufs = {"qbar": torch.empty((B, H, nqb, D), dtype=f32, device=dev),
+            "kbar": torch.empty((B, H, nkb, D), dtype=f32, device=dev),
+            "S": torch.empty((B, H, nqb, nkb), dtype=f32, device=dev),
+            "cnt": torch.empty((B, H, nqb), dtype=i32, device=dev),
+            "idx": torch.empty((B, H, nqb, kept), dtype=i32, device=dev),
+            "o": torch.empty_like(qd), "lse": torch.empty((B, H, Nq), dtype=f32, device=dev)}
+
+    def scale():
+        sp.block_means(qd, out=bufs["qbar"])
+        sp.block_means(kd, out=bufs["kbar"])
+        sp.block_scores(bufs["qbar"], bufs["kbar"], out=bufs["S"])
+        sp.select_blocks(bufs["S"], F, 0.1875, max_kept=kept, kv_count=bufs["cnt"],
+                         kv_index=bufs["idx"])
+        sp.block_sparse_attn_fwd(qd, kd, vd, bufs["cnt"], bufs["idx"], out=bufs["o"],
+                                 lse=bufs["lse"])
+
+    scale()
+    torch.cuda.synchronize()
+    eager = {n: t.clone() for n, t in bufs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm the capture stream once
+        scale()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        scale()
+    for rep in range(3):
+        for t in bufs.values():
+            t.zero_()                       # replays must rewrite everything
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in bufs.items():
+            assert torch.equal(t, eager[n]), (rep, n)
+        scale()                             # eager work between replays
+        torch.cuda.synchronize()
