@@ -52,13 +52,13 @@ def selected_flops(kv_count, kv_index, Nq, Nk, D, block=128):
     return int(4 * D * (nq * keys).sum())
 
 
-def stage_bytes(w, kept):
+def stage_bytes(w, kept, nqb, nkb):
     """Algorithmic bytes of means(Q) + means(K) + scores + select."""
     el = 2 if w.dtype == "bf16" else 4
     BH = w.B * w.H
     qk = BH * (w.Nq + w.Nk) * w.D * el
-    means = 2 * BH * (w.nqb + w.nkb) * w.D * 4
-    index = BH * w.nqb * (4 * kept + 4)
+    means = 2 * BH * (nqb + nkb) * w.D * 4
+    index = BH * nqb * (4 * kept + 4)
     return qk + means + index
 
 
@@ -175,6 +175,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline sample")
+    ap.add_argument("--block", type=int, default=128, choices=[32, 64, 128],
+                    help="block size in tokens (the pages use 128)")
     ap.add_argument("--fused", action="store_true",
                     help="scores and selection in one launch (scores stay on chip) instead of two")
     ap.add_argument("--graph", action="store_true",
@@ -218,15 +220,17 @@ def main():
 
     q, k, v = dev_t(x["q"]), dev_t(x["k"]), dev_t(x["v"])
     B, H, D = w.B, w.H, w.D
-    F = sp.forced_blocks(w.n_forced_tokens)
-    kept = sp.kept_blocks(w.nkb, F, w.density)
+    blk = args.block
+    nqb, nkb = -(-w.Nq // blk), -(-w.Nk // blk)
+    F = sp.forced_blocks(w.n_forced_tokens, blk)
+    kept = sp.kept_blocks(nkb, F, w.density)
     f32, i32 = torch.float32, torch.int32
-    qbar = torch.empty((B, H, w.nqb, D), dtype=f32, device=dev)
-    kbar = torch.empty((B, H, w.nkb, D), dtype=f32, device=dev)
-    fused = args.fused and w.nkb <= sp.FUSED_MAX_NKB
-    S = None if fused else torch.empty((B, H, w.nqb, w.nkb), dtype=f32, device=dev)
-    cnt = torch.empty((B, H, w.nqb), dtype=i32, device=dev)
-    idx = torch.empty((B, H, w.nqb, max(1, kept)), dtype=i32, device=dev)
+    qbar = torch.empty((B, H, nqb, D), dtype=f32, device=dev)
+    kbar = torch.empty((B, H, nkb, D), dtype=f32, device=dev)
+    fused = args.fused and nkb <= sp.FUSED_MAX_NKB
+    S = None if fused else torch.empty((B, H, nqb, nkb), dtype=f32, device=dev)
+    cnt = torch.empty((B, H, nqb), dtype=i32, device=dev)
+    idx = torch.empty((B, H, nqb, max(1, kept)), dtype=i32, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, w.Nq), dtype=f32, device=dev)
     stream = torch.cuda.current_stream()
@@ -234,19 +238,19 @@ def main():
 
     if fused:
         names = ["means_q", "means_k", "scores_select", "attn"]
-        calls = [lambda: sp.block_means(q, out=qbar),
-                 lambda: sp.block_means(k, out=kbar),
+        calls = [lambda: sp.block_means(q, blk, out=qbar),
+                 lambda: sp.block_means(k, blk, out=kbar),
                  lambda: sp.select_blocks_from_means(qbar, kbar, F, w.density, max_kept=kept,
                                                      kv_count=cnt, kv_index=idx),
-                 lambda: sp.block_sparse_attn_fwd(q, k, v, cnt, idx, out=o, lse=lse)]
+                 lambda: sp.block_sparse_attn_fwd(q, k, v, cnt, idx, block=blk, out=o, lse=lse)]
     else:
         names = ["means_q", "means_k", "scores", "select", "attn"]
-        calls = [lambda: sp.block_means(q, out=qbar),
-                 lambda: sp.block_means(k, out=kbar),
+        calls = [lambda: sp.block_means(q, blk, out=qbar),
+                 lambda: sp.block_means(k, blk, out=kbar),
                  lambda: sp.block_scores(qbar, kbar, out=S),
                  lambda: sp.select_blocks(S, F, w.density, max_kept=kept, kv_count=cnt,
                                           kv_index=idx),
-                 lambda: sp.block_sparse_attn_fwd(q, k, v, cnt, idx, out=o, lse=lse)]
+                 lambda: sp.block_sparse_attn_fwd(q, k, v, cnt, idx, block=blk, out=o, lse=lse)]
 
     def step(ev=None):
         for i, c in enumerate(calls):
@@ -315,21 +319,21 @@ def main():
 
     kv_count = cnt.cpu().numpy()
     kv_index = idx.cpu().numpy()
-    flops = selected_flops(kv_count, kv_index, w.Nq, w.Nk, D)
+    flops = selected_flops(kv_count, kv_index, w.Nq, w.Nk, D, blk)
     attn_tflops = flops / (stage_ms["attn"] * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
     sel_ms = sum(stage_ms[n] for n in names[:-1])
-    sbytes = stage_bytes(w, kept)
+    sbytes = stage_bytes(w, kept, nqb, nkb)
     dense_flops = 4 * D * w.Nq * w.Nk * B * H
     traffic = traffic_for_attention(w.name)
 
     diag = None
-    if not args.no_diagnostics:
+    if not args.no_diagnostics and blk == 128:
         log("[bench] retained-attention-mass diagnostic")
         diag = mass_diagnostic(sp, torch, x, w, q, k, v, cnt, idx, F, kept)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and blk == 128:
         log(f"[bench] CPU baseline (oracle, ~{args.cpu_budget:.0f} s)")
         cpu = cpu_baseline(x, w, F, args.cpu_budget)
 
@@ -346,7 +350,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) + per-block offsets; see workloads/)",
-        "config": {**w.describe(), "kept_blocks": kept, "n_forced_blocks": F,
+        "config": {**w.describe(), "block": blk, "kept_blocks": kept, "n_forced_blocks": F,
                    "selected_tflop": flops / 1e12, "dense_tflop": dense_flops / 1e12,
                    "cache": "cold" if args.cold else "warm",
                    "score_select": "fused" if fused else "two-step"},

@@ -63,7 +63,7 @@ sparstar_status check_bhnd(const char* fn, int64_t B, int64_t H, int64_t N, int6
 
 sparstar_status check_block(const char* fn, int64_t block) {
   if (block < 1) return invalid(fn, "block must be >= 1");
-  if (block != kBlock) return unsupported(fn, "only block == 128 is implemented");
+  if (!block_supported(block)) return unsupported(fn, "block must be 32, 64 or 128");
   return SPARSTAR_OK;
 }
 
@@ -105,7 +105,7 @@ sparstar_status sparstar_block_means(const void* x, sparstar_dtype dtype, int64_
   sparstar_status st = check_bhnd(fn, B, H, N, D);
   if (st != SPARSTAR_OK) return st;
   if ((st = check_block(fn, block)) != SPARSTAR_OK) return st;
-  return launch_block_means(x, dtype, B * H, N, D, out, static_cast<hipStream_t>(stream));
+  return launch_block_means(x, dtype, B * H, N, D, block, out, static_cast<hipStream_t>(stream));
 }
 
 sparstar_status sparstar_block_scores(const float* qbar, const float* kbar, int64_t B, int64_t H,
@@ -212,15 +212,15 @@ sparstar_status sparstar_block_sparse_attn_fwd(const void* q, const void* k, con
   if ((st = check_bhnd(fn, B, H, Nk, D)) != SPARSTAR_OK) return st;
   if ((st = check_block(fn, block)) != SPARSTAR_OK) return st;
   if (!std::isfinite(scale) || !(scale > 0.f)) return invalid(fn, "scale must be finite and > 0");
-  const int64_t nqb = (Nq + kBlock - 1) / kBlock;
+  const int64_t nqb = (Nq + block - 1) / block;
   if (B * H > kMaxI32 / nqb) return invalid(fn, "B*H*nqb too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == SPARSTAR_BF16)
     return launch_attn_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                static_cast<const uint16_t*>(v), B * H, Nq, Nk, D, kv_count,
+                                static_cast<const uint16_t*>(v), B * H, Nq, Nk, D, block, kv_count,
                                 kv_index, max_kept, scale, static_cast<uint16_t*>(o), lse, s);
   return launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                             static_cast<const float*>(v), B * H, Nq, Nk, D, kv_count, kv_index,
+                             static_cast<const float*>(v), B * H, Nq, Nk, D, block, kv_count, kv_index,
                              max_kept, scale, static_cast<float*>(o), lse, s);
 }
 

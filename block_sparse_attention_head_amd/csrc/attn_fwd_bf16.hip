@@ -5,10 +5,11 @@
 // runs over the valid keys of those blocks.
 //
 // Design (gfx950, wave64):
-//  * One workgroup per (b*h, query block) = 128 queries, 4 waves x 32
-//    queries; two workgroups per CU (two waves per SIMD), so one wave's
-//    matrix work overlaps the other's vector work.  Every row keeps the same
-//    number of blocks, so the grid is evenly loaded.
+//  * One workgroup per (b*h, query block) = kBlock queries, kBlock / 32
+//    waves x 32 queries (128-token blocks: 4 waves, two workgroups per CU,
+//    two waves per SIMD, so one wave's matrix work overlaps the other's
+//    vector work; 64- and 32-token blocks use 32-key tiles).  Every row keeps
+//    the same number of blocks, so the grid is evenly loaded.
 //  * Grid order: all XCDs work on the same head at a time (its K/V then
 //    stays in the MALL), and each XCD takes a contiguous run of that head's
 //    query blocks (neighbouring query blocks, which tend to select the same
@@ -49,7 +50,6 @@
 namespace sparstar {
 namespace {
 
-constexpr int kThreads = 256;
 #ifndef SPARSTAR_ATTN_BK
 #define SPARSTAR_ATTN_BK 64
 #endif
@@ -59,7 +59,11 @@ constexpr int kThreads = 256;
 #ifndef SPARSTAR_ATTN_XCD_MAP
 #define SPARSTAR_ATTN_XCD_MAP 1
 #endif
-constexpr int kBK = SPARSTAR_ATTN_BK;      // keys per LDS tile (32 or 64)
+// Keys per LDS tile: SPARSTAR_ATTN_BK (64) for 128-token blocks, 32 for the
+// smaller blocks (whose workgroups have fewer waves, so a smaller ring keeps
+// more workgroups per CU).
+template <int kBlock>
+constexpr int tile_keys_of() { return kBlock >= 128 ? SPARSTAR_ATTN_BK : 32; }
 constexpr int kXcds = 8;                   // XCDs of an MI355X; workgroups go round-robin
 // Weights exp2(s - m_ref) may grow up to a row sum of 2^16 before the
 // reference max is moved (fp32 accumulators and bf16 weights hold that
@@ -93,18 +97,20 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);                // 8 chunks, 2 rows per 256 B
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd_bf16_kernel(
+template <int D, int kBlock>
+__global__ __launch_bounds__(64 * (kBlock / 32), SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int Nq, int Nk, int nqb, int BH,
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_index, int max_kept,
     float sl2, uint16_t* __restrict__ o, float* __restrict__ lse) {
 #if defined(__HIP_DEVICE_COMPILE__)  // buffer-resource builtins exist only in the device pass
+  constexpr int kNW = kBlock / 32;            // waves: 32 queries each
+  constexpr int kBK = tile_keys_of<kBlock>();
   constexpr int ROWB = 2 * D;                 // bytes per token row
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int TILEB = kBK * ROWB;           // bytes per K (or V) tile
   constexpr int RPI = 1024 / ROWB;            // rows per 1 KB wave-wide DMA instruction
-  constexpr int DPW = TILEB / 1024 / (kThreads / 64);  // DMAs per wave per tensor
+  constexpr int DPW = TILEB / 1024 / kNW;     // DMAs per wave per tensor
   constexpr int TPB = kBlock / kBK;           // tiles per selected block
   constexpr int KT = kBK / 32;                // 32-key score sub-tiles per tile
   constexpr int NC = kBK / 16;                // 16-key P*V steps per tile
@@ -188,12 +194,12 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
   };
 
   // DMA geometry: wave w's m-th transfer fills 1 KB = LDS rows [RPI*u, RPI*u + RPI),
-  // u = 4*m + w; lane l lands in slot l % CPR of row RPI*u + l / CPR and so
+  // u = kNW*m + w; lane l lands in slot l % CPR of row RPI*u + l / CPR and so
   // fetches global chunk (slot ^ swizzle(row)).
   int dma_row[DPW], dma_off[DPW];
 #pragma unroll
   for (int m = 0; m < DPW; ++m) {
-    dma_row[m] = RPI * (4 * m + w) + l / CPR;
+    dma_row[m] = RPI * (kNW * m + w) + l / CPR;
     dma_off[m] = dma_row[m] * ROWB + 16 * ((l % CPR) ^ chunk_swizzle<D>(dma_row[m]));
   }
   // Every tile issues the same 2 * DPW transfers per wave; a tile with no
@@ -206,7 +212,7 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
     if (nv == kBK) {   // whole tile valid: scalar tile offset + constant lane offsets
 #pragma unroll
       for (int m = 0; m < DPW; ++m) {
-        const int u = 4 * m + w;
+        const int u = kNW * m + w;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + 1024 * u), 16,
                                                  dma_off[m], key0 * ROWB, 0, SPARSTAR_ATTN_KV_CPOL);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + 1024 * u), 16,
@@ -215,7 +221,7 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
     } else {           // partial tile: rows past Nk re-read row Nk-1 (finite, masked later)
 #pragma unroll
       for (int m = 0; m < DPW; ++m) {
-        const int u = 4 * m + w;
+        const int u = kNW * m + w;
         const int rr = min(base + dma_row[m], Nk - 1);
         const int off = rr * ROWB + (dma_off[m] - dma_row[m] * ROWB);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + 1024 * u), 16,
@@ -371,14 +377,12 @@ __global__ __launch_bounds__(kThreads, SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd
 #endif
 }
 
-}  // namespace
-
-sparstar_status launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     int64_t BH, int64_t Nq, int64_t Nk, int64_t D,
-                                     const int32_t* kv_count, const int32_t* kv_index,
-                                     int64_t max_kept, float scale, uint16_t* o, float* lse,
-                                     hipStream_t s) {
-  const int64_t nqb = (Nq + kBlock - 1) / kBlock;
+template <int B>
+sparstar_status launch_b(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
+                         int64_t Nq, int64_t Nk, int64_t D, const int32_t* kv_count,
+                         const int32_t* kv_index, int64_t max_kept, float scale, uint16_t* o,
+                         float* lse, hipStream_t s) {
+  const int64_t nqb = (Nq + B - 1) / B;
 #if SPARSTAR_ATTN_XCD_MAP
   const int64_t launches = BH * ((nqb + kXcds - 1) / kXcds) * kXcds;
 #else
@@ -388,15 +392,29 @@ sparstar_status launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const
     set_error("sparstar_block_sparse_attn_fwd: grid too large");
     return SPARSTAR_ERR_INVALID_ARGUMENT;
   }
-  const dim3 grid(static_cast<uint32_t>(launches)), block(kThreads);
+  const dim3 grid(static_cast<uint32_t>(launches)), block(64 * (B / 32));
   const float sl2 = scale * 1.4426950408889634f;
   if (D == 128)
-    attn_fwd_bf16_kernel<128><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, (int)BH,
-                                                     kv_count, kv_index, (int)max_kept, sl2, o, lse);
+    attn_fwd_bf16_kernel<128, B><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, (int)BH,
+                                                        kv_count, kv_index, (int)max_kept, sl2, o, lse);
   else
-    attn_fwd_bf16_kernel<64><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, (int)BH,
-                                                    kv_count, kv_index, (int)max_kept, sl2, o, lse);
+    attn_fwd_bf16_kernel<64, B><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, (int)BH,
+                                                       kv_count, kv_index, (int)max_kept, sl2, o, lse);
   return check_launch("sparstar_block_sparse_attn_fwd");
+}
+
+}  // namespace
+
+sparstar_status launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t block,
+                                     const int32_t* kv_count, const int32_t* kv_index,
+                                     int64_t max_kept, float scale, uint16_t* o, float* lse,
+                                     hipStream_t s) {
+  if (block == 32)
+    return launch_b<32>(q, k, v, BH, Nq, Nk, D, kv_count, kv_index, max_kept, scale, o, lse, s);
+  if (block == 64)
+    return launch_b<64>(q, k, v, BH, Nq, Nk, D, kv_count, kv_index, max_kept, scale, o, lse, s);
+  return launch_b<128>(q, k, v, BH, Nq, Nk, D, kv_count, kv_index, max_kept, scale, o, lse, s);
 }
 
 }  // namespace sparstar

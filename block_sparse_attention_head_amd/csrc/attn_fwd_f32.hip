@@ -3,7 +3,7 @@
 // Same operation as the bf16 MFMA kernel (forward attention over the kept
 // key blocks of each query block, SparSTAR review "What carries the
 // argument"), for float32 workloads where exact float32 products are wanted.
-// One workgroup per (b*h, query block): 256 threads, two per query, each
+// One workgroup per (b*h, query block): 2 * kBlock threads, two per query, each
 // owning half of the head dimension of q and of the output.  Key/value tiles
 // of 32 tokens are staged through LDS; the softmax is the usual online
 // (running max and sum) form.
@@ -14,16 +14,16 @@
 namespace sparstar {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kTileK = 32;
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
+template <int D, int kBlock>
+__global__ __launch_bounds__(2 * kBlock) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     int Nq, int Nk, int nqb, const int32_t* __restrict__ kv_count,
     const int32_t* __restrict__ kv_index, int max_kept, float scale_log2, float* __restrict__ o,
     float* __restrict__ lse) {
   constexpr int DH = D / 2;
+  constexpr int kThreads = 2 * kBlock;
   __shared__ float ks[kTileK][D];
   __shared__ float vs[kTileK][D];
 
@@ -107,22 +107,34 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_f32_kernel(
   }
 }
 
+template <int B>
+sparstar_status launch_b(const float* q, const float* k, const float* v, int64_t BH, int64_t Nq,
+                         int64_t Nk, int64_t D, const int32_t* kv_count, const int32_t* kv_index,
+                         int64_t max_kept, float scale, float* o, float* lse, hipStream_t s) {
+  const int64_t nqb = (Nq + B - 1) / B;
+  const dim3 grid(static_cast<uint32_t>(BH * nqb)), block(2 * B);
+  const float sl2 = scale * 1.4426950408889634f;
+  if (D == 128)
+    attn_fwd_f32_kernel<128, B><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, kv_count,
+                                                       kv_index, (int)max_kept, sl2, o, lse);
+  else
+    attn_fwd_f32_kernel<64, B><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, kv_count,
+                                                      kv_index, (int)max_kept, sl2, o, lse);
+  return check_launch("sparstar_block_sparse_attn_fwd");
+}
+
 }  // namespace
 
 sparstar_status launch_attn_fwd_f32(const float* q, const float* k, const float* v, int64_t BH,
-                                    int64_t Nq, int64_t Nk, int64_t D, const int32_t* kv_count,
-                                    const int32_t* kv_index, int64_t max_kept, float scale,
-                                    float* o, float* lse, hipStream_t s) {
-  const int64_t nqb = (Nq + kBlock - 1) / kBlock;
-  const dim3 grid(static_cast<uint32_t>(BH * nqb)), block(kThreads);
-  const float sl2 = scale * 1.4426950408889634f;
-  if (D == 128)
-    attn_fwd_f32_kernel<128><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, kv_count,
-                                                    kv_index, (int)max_kept, sl2, o, lse);
-  else
-    attn_fwd_f32_kernel<64><<<grid, block, 0, s>>>(q, k, v, (int)Nq, (int)Nk, (int)nqb, kv_count,
-                                                   kv_index, (int)max_kept, sl2, o, lse);
-  return check_launch("sparstar_block_sparse_attn_fwd");
+                                    int64_t Nq, int64_t Nk, int64_t D, int64_t block,
+                                    const int32_t* kv_count, const int32_t* kv_index,
+                                    int64_t max_kept, float scale, float* o, float* lse,
+                                    hipStream_t s) {
+  if (block == 32)
+    return launch_b<32>(q, k, v, BH, Nq, Nk, D, kv_count, kv_index, max_kept, scale, o, lse, s);
+  if (block == 64)
+    return launch_b<64>(q, k, v, BH, Nq, Nk, D, kv_count, kv_index, max_kept, scale, o, lse, s);
+  return launch_b<128>(q, k, v, BH, Nq, Nk, D, kv_count, kv_index, max_kept, scale, o, lse, s);
 }
 
 }  // namespace sparstar

@@ -1,7 +1,8 @@
-// Block means of Q or K over contiguous 128-token blocks (SparSTAR review,
-// "What carries the argument": block-averaged query and key vectors).
+// Block means of Q or K over contiguous blocks of kBlock tokens (SparSTAR
+// review, "What carries the argument": block-averaged query and key vectors
+// over 128-token blocks; 32 and 64 are instantiated as well).
 //
-// One workgroup of 256 threads per (b*h, block): the 128 x D slab is one
+// One workgroup of 256 threads per (b*h, block): the kBlock x D slab is one
 // contiguous chunk of HBM, read once with 16-byte loads by consecutive
 // threads (fully coalesced).  Each thread sums its rows column-wise in
 // registers; the per-thread partials meet in LDS as float64 and are added in
@@ -14,7 +15,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <int D, bool kBf16>
+template <int D, bool kBf16, int kBlock>
 __global__ __launch_bounds__(kThreads) void block_means_kernel(const void* __restrict__ xv,
                                                                int N, int nb,
                                                                float* __restrict__ out) {
@@ -83,11 +84,10 @@ __global__ __launch_bounds__(kThreads) void block_means_kernel(const void* __res
   }
 }
 
-}  // namespace
-
-sparstar_status launch_block_means(const void* x, sparstar_dtype dt, int64_t BH, int64_t N,
-                                   int64_t D, float* out, hipStream_t s) {
-  const int64_t nb = (N + kBlock - 1) / kBlock;
+template <int B>
+sparstar_status launch_b(const void* x, sparstar_dtype dt, int64_t BH, int64_t N, int64_t D,
+                         float* out, hipStream_t s) {
+  const int64_t nb = (N + B - 1) / B;
   if (BH * nb > 2147483647LL) {
     set_error("sparstar_block_means: B*H*nblocks exceeds the grid limit");
     return SPARSTAR_ERR_INVALID_ARGUMENT;
@@ -95,13 +95,22 @@ sparstar_status launch_block_means(const void* x, sparstar_dtype dt, int64_t BH,
   const dim3 grid(static_cast<uint32_t>(BH * nb)), block(kThreads);
   const int n = static_cast<int>(N), nbi = static_cast<int>(nb);
   if (dt == SPARSTAR_BF16) {
-    if (D == 128) block_means_kernel<128, true><<<grid, block, 0, s>>>(x, n, nbi, out);
-    else block_means_kernel<64, true><<<grid, block, 0, s>>>(x, n, nbi, out);
+    if (D == 128) block_means_kernel<128, true, B><<<grid, block, 0, s>>>(x, n, nbi, out);
+    else block_means_kernel<64, true, B><<<grid, block, 0, s>>>(x, n, nbi, out);
   } else {
-    if (D == 128) block_means_kernel<128, false><<<grid, block, 0, s>>>(x, n, nbi, out);
-    else block_means_kernel<64, false><<<grid, block, 0, s>>>(x, n, nbi, out);
+    if (D == 128) block_means_kernel<128, false, B><<<grid, block, 0, s>>>(x, n, nbi, out);
+    else block_means_kernel<64, false, B><<<grid, block, 0, s>>>(x, n, nbi, out);
   }
   return check_launch("sparstar_block_means");
+}
+
+}  // namespace
+
+sparstar_status launch_block_means(const void* x, sparstar_dtype dt, int64_t BH, int64_t N,
+                                   int64_t D, int64_t block, float* out, hipStream_t s) {
+  if (block == 32) return launch_b<32>(x, dt, BH, N, D, out, s);
+  if (block == 64) return launch_b<64>(x, dt, BH, N, D, out, s);
+  return launch_b<128>(x, dt, BH, N, D, out, s);
 }
 
 }  // namespace sparstar

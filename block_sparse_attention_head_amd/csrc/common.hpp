@@ -19,7 +19,7 @@ void clear_error();
 // SPARSTAR_ERR_HIP after checking hipGetLastError; arguments are validated
 // by the callers in api.hip.
 sparstar_status launch_block_means(const void* x, sparstar_dtype dt, int64_t BH, int64_t N,
-                                   int64_t D, float* out, hipStream_t s);
+                                   int64_t D, int64_t block, float* out, hipStream_t s);
 sparstar_status launch_block_scores(const float* qbar, const float* kbar, int64_t BH,
                                     int64_t nqb, int64_t nkb, int64_t D, float tau, float* S,
                                     hipStream_t s);
@@ -33,12 +33,13 @@ sparstar_status launch_scores_select(const float* qbar, const float* kbar, int64
 // Largest nkb the fused score + selection kernel takes (its score rows live in LDS).
 int64_t fused_select_max_nkb();
 sparstar_status launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     int64_t BH, int64_t Nq, int64_t Nk, int64_t D,
+                                     int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t block,
                                      const int32_t* kv_count, const int32_t* kv_index,
                                      int64_t max_kept, float scale, uint16_t* o, float* lse,
                                      hipStream_t s);
 sparstar_status launch_attn_fwd_f32(const float* q, const float* k, const float* v, int64_t BH,
-                                    int64_t Nq, int64_t Nk, int64_t D, const int32_t* kv_count,
+                                    int64_t Nq, int64_t Nk, int64_t D, int64_t block,
+                                    const int32_t* kv_count,
                                     const int32_t* kv_index, int64_t max_kept, float scale,
                                     float* o, float* lse, hipStream_t s);
 
@@ -50,7 +51,8 @@ sparstar_status check_launch(const char* what);
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------
-constexpr int kBlock = 128;  // key/query block size (tokens)
+// Block sizes (tokens) the kernels are instantiated for; 128 is the pages'.
+inline bool block_supported(int64_t b) { return b == 32 || b == 64 || b == 128; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -275,10 +275,11 @@ __global__ __launch_bounds__(64 * kFusedWaves) void scores_select_kernel(
 
 // Keys-per-lane instantiations: ceil(nkb / 64) rounded up to one of these.
 #define SPARSTAR_FOR_EACH_C(X) X(1) X(2) X(3) X(4) X(6) X(8) X(10) X(12) X(14) X(16) X(18) X(20) X(24) X(28) X(32)
+#define SPARSTAR_FOR_EACH_C_LARGE(X) X(40) X(48) X(56) X(64) X(72)
 
 int keys_per_lane(int64_t nkb) {
   const int64_t c = (nkb + 63) / 64;
-  const int table[] = {1, 2, 3, 4, 6, 8, 10, 12, 14, 16, 18, 20, 24, 28, 32};
+  const int table[] = {1, 2, 3, 4, 6, 8, 10, 12, 14, 16, 18, 20, 24, 28, 32, 40, 48, 56, 64, 72};
   for (int t : table)
     if (c <= t) return t;
   return 0;
@@ -300,6 +301,7 @@ sparstar_status launch_select_blocks(const float* S, int64_t rows, int64_t nkb, 
 #define SPARSTAR_SELECT_CASE(CC) \
   case CC: select_kernel<CC><<<grid, block, 0, s>>>(S, rows, n, f, kk, kv_count, kv_index, mk); break;
     SPARSTAR_FOR_EACH_C(SPARSTAR_SELECT_CASE)
+    SPARSTAR_FOR_EACH_C_LARGE(SPARSTAR_SELECT_CASE)
 #undef SPARSTAR_SELECT_CASE
     default: select_kernel<0><<<grid, block, 0, s>>>(S, rows, n, f, kk, kv_count, kv_index, mk);
   }

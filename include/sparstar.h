@@ -46,7 +46,7 @@ extern "C" {
 typedef enum {
   SPARSTAR_OK = 0,
   SPARSTAR_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, bad density, ... */
-  SPARSTAR_ERR_UNSUPPORTED = 2,      /* valid but not implemented (block != 128, D not 64/128) */
+  SPARSTAR_ERR_UNSUPPORTED = 2,      /* valid but not implemented (block not 32/64/128, D not 64/128) */
   SPARSTAR_ERR_HIP = 3               /* the HIP runtime refused a launch */
 } sparstar_status;
 
@@ -55,8 +55,11 @@ typedef enum {
   SPARSTAR_BF16 = 1  /* bfloat16 bit patterns (uint16) */
 } sparstar_dtype;
 
-/* Block size the library supports: the review's "Block size b = 128 tokens"
- * ("Assumptions & free parameters"). */
+/* The pages' block size: the review's "Block size b = 128 tokens"
+ * ("Assumptions & free parameters").  The means and attention entry points
+ * also take block = 64 or 32: the review notes that smaller blocks improve
+ * fidelity but had no efficient kernel in the authors' environment
+ * ("Assumptions & free parameters", "Referee Report" minor comment 4). */
 #define SPARSTAR_BLOCK 128
 
 /*
@@ -67,7 +70,7 @@ typedef enum {
  *        [i*block, min((i+1)*block, N)); a partial last block is divided by
  *        its own token count.  Sums are accumulated exactly enough that the
  *        result is the fp32 rounding of the exact mean up to ~1 ulp.
- * Requires block == 128, D in {64,128}, N >= 1.
+ * Requires block in {32, 64, 128}, D in {64,128}, N >= 1.
  */
 sparstar_status sparstar_block_means(const void* x, sparstar_dtype dtype, int64_t B, int64_t H,
                                      int64_t N, int64_t D, int64_t block, float* out,
@@ -139,8 +142,9 @@ sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float
  *   q [B,H,Nq,D], k, v [B,H,Nk,D] of `dtype`; o [B,H,Nq,D] of `dtype`;
  *   lse [B,H,Nq] float32, may be NULL.
  * bf16 inputs run on bf16 MFMA with float32 accumulation and a float32
- * online softmax; float32 inputs run in float32 throughout.
- * Requires block == 128, D in {64,128}.
+ * online softmax; float32 inputs run in float32 throughout.  Query block i
+ * is tokens [i*block, (i+1)*block) and key block j tokens [j*block, ...).
+ * Requires block in {32, 64, 128}, D in {64,128}.
  */
 sparstar_status sparstar_block_sparse_attn_fwd(const void* q, const void* k, const void* v,
                                                sparstar_dtype dtype, int64_t B, int64_t H,

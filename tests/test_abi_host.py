@@ -82,7 +82,8 @@ def test_means_validation():
     f = _lib().sparstar_block_means
     _err(f(NULL, 1, 1, 1, 128, 128, 128, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "null")
     _err(f(FAKE, 1, 1, 1, 128, 96, 128, FAKE, NULL), sp.ERR_UNSUPPORTED, "D must be")
-    _err(f(FAKE, 1, 1, 1, 128, 128, 64, FAKE, NULL), sp.ERR_UNSUPPORTED, "block")
+    _err(f(FAKE, 1, 1, 1, 128, 128, 96, FAKE, NULL), sp.ERR_UNSUPPORTED, "block")
+    _err(f(FAKE, 1, 1, 1, 128, 128, 16, FAKE, NULL), sp.ERR_UNSUPPORTED, "block")
     _err(f(FAKE, 1, 0, 1, 128, 128, 128, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "B and H")
     _err(f(FAKE, 1, 1, 1, 0, 128, 128, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "sequence")
     _err(f(FAKE, 7, 1, 1, 128, 128, 128, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "dtype")
@@ -159,6 +160,7 @@ def test_attn_validation():
     _err(call(idx=NULL), sp.ERR_INVALID_ARGUMENT, "kv_index")
     _err(call(D=80), sp.ERR_UNSUPPORTED, "D must be")
     _err(call(block=256), sp.ERR_UNSUPPORTED, "block")
+    _err(call(block=48), sp.ERR_UNSUPPORTED, "block")
     _err(call(Nk=0), sp.ERR_INVALID_ARGUMENT, "sequence")
     _err(call(scale=0.0), sp.ERR_INVALID_ARGUMENT, "scale")
     _err(call(scale=float("nan")), sp.ERR_INVALID_ARGUMENT, "scale")

@@ -62,6 +62,7 @@ SEL_CASES = [
     (200, 10, 1.0, "normal"), (64, 0, 0.0, "normal"), (65, 65, 0.5, "normal"),
     (2048, 4, 0.09375, "ties"), (2100, 4, 0.1, "normal"), (3000, 7, 0.3, "nan"),
     (1, 0, 1.0, "normal"), (500, 3, 0.2, "inf"), (257, 2, 0.33, "zeros"),
+    (2300, 4, 0.09375, "normal"), (4516, 4, 0.09375, "ties"), (4700, 9, 0.2, "nan"),
 ]
 
 
