@@ -317,6 +317,27 @@ def main():
     stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
                 for i, n in enumerate(names)}
 
+    # the same steps with L2 and MALL overwritten first (512 MiB) before each
+    cold = None
+    if not args.cold:
+        log("[bench] cold-cache pass")
+        fl = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+              for _ in range(min(args.steps, 5))]
+        for e in ce:
+            fl.fill_(0)
+            step(e)
+        torch.cuda.synchronize()
+        c_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ce]))
+                for i, n in enumerate(names)}
+        c_sel = sum(c_ms[n] for n in names[:-1])
+        cold = {"ms_per_step": round(sum(c_ms.values()), 4),
+                "selection_us": round(c_sel * 1e3, 2), "attn_us": round(c_ms["attn"] * 1e3, 2),
+                "selection_frac_hbm": round(stage_bytes(w, kept, nqb, nkb) / (c_sel * 1e-3) / 1e9
+                                            / PEAK_HBM_GBPS, 4),
+                "steps": len(ce)}
+        del fl
+
     kv_count = cnt.cpu().numpy()
     kv_index = idx.cpu().numpy()
     flops = selected_flops(kv_count, kv_index, w.Nq, w.Nk, D, blk)
@@ -359,6 +380,7 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "diagnostics": diag,
+        "cold_cache": cold,
         "stages": {
             **{f"{n}_us": round(stage_ms[n] * 1e3, 2) for n in names},
             "attn_tflops": round(attn_tflops, 2),
