@@ -184,3 +184,18 @@ def test_product_path_does_not_import_oracle():
             if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "oracle" not in text.lower(), fn
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="only where no GPU is visible: the call must fail at the launch")
+def test_launch_failure_is_reported_without_a_gpu():
+    """Valid arguments but no GPU: the launch fails, the call returns
+    SPARSTAR_ERR_HIP with a message, and the next call clears it."""
+    st = _lib().sparstar_block_means(FAKE, 1, 1, 1, 256, 128, 128, FAKE, NULL)
+    assert st == sp.ERR_HIP, (st, sp.last_error())
+    assert "sparstar_block_means" in sp.last_error()
+    st = _lib().sparstar_block_scores(FAKE, FAKE, 1, 1, 4, 4, 128, 0.1, FAKE, NULL)
+    assert st == sp.ERR_HIP, (st, sp.last_error())
+    assert sp.last_error() != ""
+    _err(_lib().sparstar_block_means(NULL, 1, 1, 1, 128, 128, 128, FAKE, NULL),
+         sp.ERR_INVALID_ARGUMENT, "null")
