@@ -50,6 +50,8 @@
 namespace sparstar {
 namespace {
 
+// Build-time design knobs; the defaults are the measured best on MI355X
+// (64-key tiles, two waves per SIMD, XCD-aware order, default cache policy).
 #ifndef SPARSTAR_ATTN_BK
 #define SPARSTAR_ATTN_BK 64
 #endif
