@@ -30,11 +30,15 @@ Readings where the pages are silent (each also listed in the design notes):
   * ties in S go to the lower block index; NaN ranks below every number;
   * attention uses scale D^-1/2, no causal mask, only keys past Nk masked;
   * the kept index list is ascending; a row with nothing kept yields O = 0
-    and LSE = -inf.
+    and LSE = -inf;
+  * mask reuse (the ablation baseline): blocks map between scales by the
+    relative position of their centre within their segment, and the reused
+    scores are ranked under the target scale's forced set and budget.
 
 Everything is float64.  bf16 inputs are decoded exactly from their bits.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 
@@ -258,6 +262,84 @@ def token_topk_bound_rows(q, k, n_forced_blocks, k_blocks, rows, block=128, scal
         elig = np.sort(p[:, f_tok:], axis=1)[:, ::-1]
         out[(b, h, i)] = forced + elig[:, :m_tok].sum(axis=1)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Mask reuse -- the ablation baseline the method is compared against
+# ([R] "Extended reading notes", "Core claim": a block selection carried over
+# from another scale, or across a clip boundary, keeps less attention mass
+# than a fresh one; [A] "Abstract (arXiv)": recomputing the selection at each
+# target scale against reusing a transferred mask).
+#
+# The pages do not say how block indices map between scales.  Reading: a
+# scale's geometry is (n_text, n_ref, n_cur); queries are the current scale
+# and keys the concatenation [text | ref | cur] (Eq. 1 order).  A block is
+# represented by the centre of its valid tokens (token t covers [t, t + 1));
+# the segment holding that centre is mapped by relative position onto the
+# same segment of the other scale, and the token found there names the block.
+# The transferred selection ranks the target scale's eligible blocks by the
+# scores of the blocks they map to, under the target scale's own forced set
+# and budget (so both selections spend the same number of blocks), with the
+# usual tie rule.
+# ---------------------------------------------------------------------------
+def _centre(j, n_tokens, block):
+    """Centre of the valid tokens of block j of an n_tokens sequence (exact)."""
+    first = j * block
+    last = min((j + 1) * block, n_tokens) - 1
+    return Fraction(first + last + 1, 2)
+
+
+def transfer_query_map(src_n_cur, dst_n_cur, block=128):
+    """For each target query block, the source query block it reuses."""
+    if src_n_cur < 1 or dst_n_cur < 1:
+        raise ValueError("both scales need at least one query token")
+    nqb_dst = -(-dst_n_cur // block)
+    out = np.empty(nqb_dst, dtype=np.int64)
+    for i in range(nqb_dst):
+        rel = _centre(i, dst_n_cur, block) / dst_n_cur
+        out[i] = math.floor(rel * src_n_cur) // block
+    return out
+
+
+def transfer_key_map(src_geom, dst_geom, block=128):
+    """For each target key block, the source key block it reuses.
+
+    src_geom, dst_geom: (n_text, n_ref, n_cur) of the two scales."""
+    src = [int(x) for x in src_geom]
+    dst = [int(x) for x in dst_geom]
+    if min(src + dst) < 0:
+        raise ValueError("segment lengths must be non-negative")
+    n_dst = sum(dst)
+    nkb_dst = -(-n_dst // block)
+    out = np.empty(nkb_dst, dtype=np.int64)
+    for j in range(nkb_dst):
+        c = _centre(j, n_dst, block)
+        start_dst = start_src = 0
+        for seg in range(3):
+            if start_dst <= c < start_dst + dst[seg]:
+                if src[seg] == 0:
+                    raise ValueError("a target segment has no counterpart in the source scale")
+                rel = (c - start_dst) / dst[seg]
+                out[j] = (start_src + math.floor(rel * src[seg])) // block
+                break
+            start_dst += dst[seg]
+            start_src += src[seg]
+    return out
+
+
+def transfer_scores(S_src, src_geom, dst_geom, block=128):
+    """S_src [..., nqb_src, nkb_src] -> the scores each target block pair reuses."""
+    qmap = transfer_query_map(int(src_geom[2]), int(dst_geom[2]), block)
+    kmap = transfer_key_map(src_geom, dst_geom, block)
+    S_src = np.asarray(S_src)
+    return S_src[..., qmap[:, None], kmap[None, :]]
+
+
+def transferred_selection(S_src, src_geom, dst_geom, n_forced, density, block=128,
+                          max_kept=None):
+    """The target scale's selection when the source scale's scores are reused."""
+    return select_blocks(transfer_scores(S_src, src_geom, dst_geom, block), n_forced,
+                         density, max_kept)
 
 
 # ---------------------------------------------------------------------------

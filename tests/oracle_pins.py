@@ -369,7 +369,92 @@ def pin_token_topk_bound(impl, seed=9):
     assert all(np.abs(u[r] - 1).max() <= 1e-12 for r in rows)
 
 
+# --- mask reuse: block maps between scales ----------------------------------
+def pin_transfer_golden(impl):
+    """Block maps worked by hand from the mask-reuse reading (tests/golden/
+    transfer_tiny.json): upsampling, downsampling, a partial last block and a
+    block straddling two segments."""
+    g = _golden("transfer_tiny.json")
+    for c in g["cases"]:
+        km = impl.transfer_key_map(c["src"], c["dst"], c["block"])
+        qm = impl.transfer_query_map(c["src"][2], c["dst"][2], c["block"])
+        assert km.tolist() == c["key_map"], (c["note"], km.tolist())
+        assert qm.tolist() == c["query_map"], (c["note"], qm.tolist())
+
+
+def pin_transfer_identity(impl, seed=10):
+    """The same geometry on both sides maps every block to itself, so the
+    reused scores are the source scores and the reused selection is the
+    fresh one (any geometry, partial blocks and straddling blocks included)."""
+    rng = np.random.default_rng(seed)
+    for geom in [(0, 0, 300), (512, 0, 1000), (512, 3600, 7000), (100, 200, 50), (1, 1, 1)]:
+        for b in (32, 128):
+            n = sum(geom)
+            assert impl.transfer_key_map(geom, geom, b).tolist() == list(range(-(-n // b)))
+            assert impl.transfer_query_map(geom[2], geom[2], b).tolist() == list(range(-(-geom[2] // b)))
+    geom = (512, 1000, 1300)
+    S = rng.standard_normal((2, 3, -(-1300 // 128), -(-2812 // 128)))
+    T = impl.transfer_scores(S, geom, geom)
+    assert np.array_equal(T, S)
+    c1, i1 = impl.transferred_selection(S, geom, geom, 4, 0.25)
+    c2, i2 = impl.select_blocks(S, 4, 0.25)
+    assert np.array_equal(c1, c2) and np.array_equal(i1, i2)
+
+
+def pin_transfer_integer_upsample(impl):
+    """Block-aligned segments scaled by an integer factor m: every source block
+    of a scaled segment is reused by exactly m consecutive target blocks (a
+    closed form), the unscaled text segment maps to itself."""
+    b = 128
+    for m in (2, 3):
+        src = (256, 3 * b, 5 * b)
+        dst = (256, 3 * b * m, 5 * b * m)
+        km = impl.transfer_key_map(src, dst, b)
+        expect = [0, 1] + [2 + j // m for j in range(3 * m)] + [5 + j // m for j in range(5 * m)]
+        assert km.tolist() == expect, (m, km.tolist())
+        qm = impl.transfer_query_map(src[2], dst[2], b)
+        assert qm.tolist() == [j // m for j in range(5 * m)]
+        # the other way round every m-th source block is taken: block m*j + m//2
+        km_down = impl.transfer_key_map(dst, src, b)
+        assert km_down.tolist() == [0, 1] + [2 + m * j + m // 2 for j in range(3)] + \
+            [2 + 3 * m + m * j + m // 2 for j in range(5)], (m, km_down.tolist())
+
+
+def pin_transfer_invariants(impl, seed=11):
+    """Random geometries: maps stay in range, never decrease, and the source
+    token they land on lies in the same segment as the target block's centre
+    (checked here by a direct scan over tokens, not by the map's arithmetic)."""
+    rng = np.random.default_rng(seed)
+    for _ in range(40):
+        b = int(rng.choice([4, 32, 128]))
+        t = int(rng.integers(0, 300))
+        src = (t, int(rng.integers(1, 2000)), int(rng.integers(1, 2000)))
+        dst = (t, int(rng.integers(1, 2000)), int(rng.integers(1, 2000)))
+        km = impl.transfer_key_map(src, dst, b)
+        qm = impl.transfer_query_map(src[2], dst[2], b)
+        assert km.size == -(-sum(dst) // b) and qm.size == -(-dst[2] // b)
+        assert km.min() >= 0 and km.max() < -(-sum(src) // b)
+        assert qm.min() >= 0 and qm.max() < -(-src[2] // b)
+        assert np.all(np.diff(km) >= 0) and np.all(np.diff(qm) >= 0)
+        seg_src = np.repeat([0, 1, 2], src)
+        seg_dst = np.repeat([0, 1, 2], dst)
+        n_dst = sum(dst)
+        for j in range(km.size):
+            lo, hi = j * b, min((j + 1) * b, n_dst)
+            # centre of [lo, hi) is (lo + hi) / 2: the token holding it
+            seg = seg_dst[(lo + hi) // 2] if (lo + hi) % 2 == 0 else seg_dst[(lo + hi - 1) // 2]
+            toks = np.arange(km[j] * b, min((km[j] + 1) * b, sum(src)))
+            assert np.any(seg_src[toks] == seg), (src, dst, b, j)
+    try:
+        impl.transfer_key_map((0, 0, 100), (0, 50, 100), 32)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a target segment with no source counterpart must be refused")
+
+
 ALL_PINS = [pin_identity, pin_means_closed_form, pin_selection_bruteforce,
             pin_ties_duplicated_blocks, pin_tiny_budget, pin_dense_equivalence,
             pin_masked_sdpa, pin_convex_hull, pin_empty_selection, pin_selected_flops,
-            pin_retained_mass, pin_token_topk_bound]
+            pin_retained_mass, pin_token_topk_bound, pin_transfer_golden,
+            pin_transfer_identity, pin_transfer_integer_upsample, pin_transfer_invariants]

@@ -49,6 +49,16 @@ MUTATIONS = {
                                    "elig = np.sort(p[:, f_tok:], axis=1)"),
     "bound-ignores-forced": ("out[(b, h, i)] = forced + elig[:, :m_tok].sum(axis=1)",
                              "out[(b, h, i)] = elig[:, :m_tok].sum(axis=1)"),
+    "transfer-centre-off-by-half": ("return Fraction(first + last + 1, 2)", "return Fraction(first + last, 2)"),
+    "transfer-block-start-not-centre": ("return Fraction(first + last + 1, 2)", "return Fraction(first)"),
+    "transfer-source-start-not-advanced": ("            start_src += src[seg]\n", "            start_src += dst[seg]\n"),
+    "transfer-relative-to-source-length": ("rel = (c - start_dst) / dst[seg]", "rel = (c - start_dst) / src[seg]"),
+    "transfer-query-map-target-size": ("out[i] = math.floor(rel * src_n_cur) // block",
+                                       "out[i] = math.floor(rel * dst_n_cur) // block"),
+    "transfer-query-rounds-up": ("out[i] = math.floor(rel * src_n_cur) // block",
+                                 "out[i] = math.ceil(rel * src_n_cur) // block"),
+    "transfer-transposed-gather": ("return S_src[..., qmap[:, None], kmap[None, :]]",
+                                   "return S_src[..., qmap[:, None], kmap[None, :]][..., ::-1]"),
     "flops-counts-padding": ("nk = int(np.minimum((blocks + 1) * block, Nk).sum() - (blocks * block).sum())",
                              "nk = int(blocks.size * block)"),
 }
