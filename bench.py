@@ -164,6 +164,71 @@ def mass_diagnostic(sp, torch, x, w, q, k, v, cnt, idx, F, kept, sample_blocks=4
     }
 
 
+def mask_reuse_diagnostic(sp, torch, w, q, k, v, F, kept, fresh_cnt, fresh_idx):
+    """The mask-reuse baseline at this scale: the selection carried over from
+    the preceding sparsified scale of the same clip, and from the same scale
+    of the preceding clip, against the fresh one (retained attention mass and
+    block overlap), plus the transfer kernel's time."""
+    import dataclasses
+    from workloads import make_inputs
+    from workloads.configs import SWEEP_SCALES, SWEEP_DENSITIES
+    if w.Nq not in SWEEP_SCALES or SWEEP_SCALES.index(w.Nq) == 0:
+        return None
+    prev = SWEEP_SCALES[SWEEP_SCALES.index(w.Nq) - 1]
+    dev = q.device
+
+    def scores_of(ws):
+        xs = make_inputs(ws)
+        qs = torch.from_numpy(xs["q"].view(np.int16)).view(torch.bfloat16).to(dev)
+        ks = torch.from_numpy(xs["k"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return sp.block_scores(sp.block_means(qs), sp.block_means(ks))
+
+    dst = (w.n_text, w.n_ref, w.n_cur)
+    sources = {
+        # preceding scale of the same clip (its reference scales with it
+        # unless it is Clip 1's fixed image reference)
+        "previous_scale": dataclasses.replace(
+            w, name=f"{w.name}-prev-scale", Nq=prev, n_cur=prev,
+            n_ref=w.n_ref if w.ref_forced else prev,
+            density=SWEEP_DENSITIES[SWEEP_SCALES.index(prev)]),
+        # the same scale of the preceding clip: an independent draw
+        "previous_clip": dataclasses.replace(w, name=f"{w.name}-prev-clip", seed=w.seed + 1),
+    }
+    fresh_mass = sp.selection_retained_mass(q, k, v, fresh_cnt, fresh_idx)
+    fc, fi = fresh_cnt.cpu().numpy(), fresh_idx.cpu().numpy()
+    out = {"fresh_mass_mean": round(float(fresh_mass.float().mean()), 5)}
+    for tag, ws in sources.items():
+        S_src = scores_of(ws)
+        src = (ws.n_text, ws.n_ref, ws.n_cur)
+        S_dst = sp.transfer_scores(S_src, src, dst)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(10):
+            sp.transfer_scores(S_src, src, dst, out=S_dst)
+        ev[1].record()
+        torch.cuda.synchronize()
+        t_us = ev[0].elapsed_time(ev[1]) * 100.0
+        nbytes = 4 * (S_dst.numel() + S_src.numel())
+        rc, ri = sp.select_blocks(S_dst, F, w.density, max_kept=kept)
+        m = sp.selection_retained_mass(q, k, v, rc, ri).float().cpu().numpy()
+        rc_np, ri_np = rc.cpu().numpy(), ri.cpu().numpy()
+        shared = 0
+        for r in range(fc.size):
+            a = fi.reshape(fc.size, -1)[r, :fc.reshape(-1)[r]]
+            b = ri_np.reshape(rc_np.size, -1)[r, :rc_np.reshape(-1)[r]]
+            shared += np.intersect1d(a[a >= F], b[b >= F]).size
+        ranked = int(np.maximum(fc.reshape(-1) - F, 0).sum())
+        out[tag] = {
+            "source": f"n_text={src[0]} n_ref={src[1]} n_cur={src[2]} (seed {ws.seed})",
+            "reused_mass_mean": round(float(m.mean()), 5),
+            "reused_mass_p05": round(float(np.quantile(m, 0.05)), 5),
+            "ranked_blocks_shared_with_fresh": round(shared / max(ranked, 1), 4),
+            "transfer_us": round(t_us, 2),
+            "transfer_gbps": round(nbytes / (t_us * 1e-6) / 1e9, 1),
+        }
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -352,6 +417,9 @@ def main():
     if not args.no_diagnostics and blk == 128:
         log("[bench] retained-attention-mass diagnostic")
         diag = mass_diagnostic(sp, torch, x, w, q, k, v, cnt, idx, F, kept)
+        if w.dtype == "bf16":
+            log("[bench] mask-reuse baseline")
+            diag["mask_reuse"] = mask_reuse_diagnostic(sp, torch, w, q, k, v, F, kept, cnt, idx)
 
     cpu = None
     if not args.no_cpu_baseline and blk == 128:

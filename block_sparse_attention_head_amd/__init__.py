@@ -9,5 +9,5 @@ from .binding import (  # noqa: F401
     BLOCK, BF16, FP32, FUSED_MAX_NKB, OK, ERR_HIP, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, LIB_PATH,
     SparstarError, block_means, block_scores, block_sparse_attn_fwd, forced_blocks,
     kept_blocks, last_error, lib, select_blocks, select_blocks_from_means, sparse_attention, version,
-    retained_mass, selection_retained_mass,
+    retained_mass, selection_retained_mass, transfer_scores, transferred_selection,
 )

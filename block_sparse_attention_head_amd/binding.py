@@ -26,6 +26,8 @@ _SIGNATURES = {
     "sparstar_block_sparse_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64,
                                                       _i64, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
     "sparstar_retained_mass": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp]),
+    "sparstar_transfer_scores": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                _i64, _vp, _vp]),
     "sparstar_forced_blocks": (_i64, [_i64, _i64]),
     "sparstar_kept_blocks": (_i64, [_i64, _i64, _f64]),
     "sparstar_last_error": (ctypes.c_char_p, []),
@@ -204,6 +206,32 @@ def retained_mass(lse_sel, lse_dense, out=None, stream=None):
     _check(lib().sparstar_retained_mass(_dev(lse_sel, "lse_sel"), _dev(lse_dense, "lse_dense"),
                                         lse_sel.numel(), _dev(out, "mass"), _stream(stream)))
     return out
+
+
+def transfer_scores(S_src, src_geom, dst_geom, block=BLOCK, out=None, stream=None):
+    """Scores of a source scale carried to a target scale (mask reuse).
+
+    src_geom, dst_geom: (n_text, n_ref, n_cur) token counts of the two scales;
+    S_src [B,H,ceil(src n_cur/block),ceil(src total/block)] fp32 ->
+    S_dst [B,H,ceil(dst n_cur/block),ceil(dst total/block)] fp32."""
+    torch = _torch()
+    B, H = S_src.shape[:2]
+    nqb = -(-int(dst_geom[2]) // block)
+    nkb = -(-sum(int(x) for x in dst_geom) // block)
+    if out is None:
+        out = torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=S_src.device)
+    _check(lib().sparstar_transfer_scores(_dev(S_src, "S_src"), B, H, block, *[int(x) for x in src_geom],
+                                          *[int(x) for x in dst_geom], _dev(out, "S_dst"),
+                                          _stream(stream)))
+    return out
+
+
+def transferred_selection(S_src, src_geom, dst_geom, n_forced_blocks, density, block=BLOCK,
+                          max_kept=None, stream=None):
+    """The target scale's selection when the source scale's scores are reused:
+    transfer_scores, then select_blocks under the target's forced set and budget."""
+    S = transfer_scores(S_src, src_geom, dst_geom, block=block, stream=stream)
+    return select_blocks(S, n_forced_blocks, density, max_kept=max_kept, stream=stream)
 
 
 def selection_retained_mass(q, k, v, kv_count, kv_index, block=BLOCK, stream=None):

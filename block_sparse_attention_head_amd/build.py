@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsparstar.so")
 SOURCES = ["api.hip", "block_means.hip", "block_scores.hip", "select_blocks.hip",
-           "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "retained_mass.hip"]
+           "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "retained_mass.hip",
+           "transfer_scores.hip"]
 ARCH = "gfx950"
 
 

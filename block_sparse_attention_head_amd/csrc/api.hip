@@ -76,7 +76,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" {
 
-int32_t sparstar_version(void) { return 10000; }
+int32_t sparstar_version(void) { return 10100; }
 
 const char* sparstar_last_error(void) { return g_err; }
 
@@ -191,6 +191,40 @@ sparstar_status sparstar_retained_mass(const float* lse_sel, const float* lse_de
   if (n == 0) return SPARSTAR_OK;
   if (!lse_sel || !lse_dense || !mass) return invalid(fn, "null pointer");
   return launch_retained_mass(lse_sel, lse_dense, n, mass, static_cast<hipStream_t>(stream));
+}
+
+sparstar_status sparstar_transfer_scores(const float* S_src, int64_t B, int64_t H, int64_t block,
+                                         int64_t src_n_text, int64_t src_n_ref, int64_t src_n_cur,
+                                         int64_t dst_n_text, int64_t dst_n_ref, int64_t dst_n_cur,
+                                         float* S_dst, void* stream) {
+  const char* fn = "sparstar_transfer_scores";
+  clear_error();
+  if (!S_src || !S_dst) return invalid(fn, "null pointer");
+  if (S_src == S_dst) return invalid(fn, "S_src and S_dst must not overlap");
+  if (B < 1 || H < 1) return invalid(fn, "B and H must be >= 1");
+  if (B > kMaxI32 / H) return invalid(fn, "B*H too large");
+  sparstar_status st;
+  if ((st = check_block(fn, block)) != SPARSTAR_OK) return st;
+  const int64_t src[3] = {src_n_text, src_n_ref, src_n_cur};
+  const int64_t dst[3] = {dst_n_text, dst_n_ref, dst_n_cur};
+  constexpr int64_t kMaxScale = int64_t(1) << 30;
+  int64_t ns = 0, nd = 0;
+  for (int k = 0; k < 3; ++k) {
+    if (src[k] < 0 || dst[k] < 0) return invalid(fn, "segment lengths must be >= 0");
+    if (src[k] >= kMaxScale || dst[k] >= kMaxScale) return invalid(fn, "a scale must hold fewer than 2^30 tokens");
+    if (dst[k] > 0 && src[k] == 0)
+      return invalid(fn, "a non-empty target segment has an empty source segment");
+    ns += src[k];
+    nd += dst[k];
+  }
+  if (ns >= kMaxScale || nd >= kMaxScale) return invalid(fn, "a scale must hold fewer than 2^30 tokens");
+  if (src_n_cur < 1 || dst_n_cur < 1) return invalid(fn, "n_cur must be >= 1 on both scales");
+  const int64_t nqs = (src_n_cur + block - 1) / block, nks = (ns + block - 1) / block;
+  const int64_t nqd = (dst_n_cur + block - 1) / block, nkd = (nd + block - 1) / block;
+  if (nqs > kMaxI32 / nks || nqd > kMaxI32 / nkd)
+    return invalid(fn, "nqb*nkb per head must fit in int32");
+  return launch_transfer_scores(S_src, B * H, block, src, dst, S_dst,
+                                static_cast<hipStream_t>(stream));
 }
 
 sparstar_status sparstar_block_sparse_attn_fwd(const void* q, const void* k, const void* v,

@@ -46,6 +46,10 @@ sparstar_status launch_attn_fwd_f32(const float* q, const float* k, const float*
 sparstar_status launch_retained_mass(const float* lse_sel, const float* lse_dense, int64_t n,
                                      float* mass, hipStream_t s);
 
+sparstar_status launch_transfer_scores(const float* S_src, int64_t BH, int64_t block,
+                                       const int64_t src_geom[3], const int64_t dst_geom[3],
+                                       float* S_dst, hipStream_t s);
+
 sparstar_status check_launch(const char* what);
 
 // ---------------------------------------------------------------------------

@@ -168,6 +168,38 @@ sparstar_status sparstar_block_sparse_attn_fwd(const void* q, const void* k, con
 sparstar_status sparstar_retained_mass(const float* lse_sel, const float* lse_dense, int64_t n,
                                        float* mass, void* stream);
 
+/*
+ * Mask reuse, the baseline the method argues against (review, "Extended
+ * reading notes" / "Core claim": a selection carried over from another scale
+ * or across a clip boundary keeps less attention mass than a fresh one;
+ * abstract: the analyses compare a selection computed anew per scale with
+ * one carried over).  Builds the target scale's score matrix from a source
+ * scale's, so that sparstar_select_blocks on it gives the transferred
+ * selection under the target scale's own forced set and budget:
+ *   S_dst[b,h,i,j] = S_src[b,h, qmap(i), kmap(j)].
+ * A scale's geometry is (n_text, n_ref, n_cur): queries are its n_cur
+ * current tokens, keys the concatenation [text | ref | cur], both cut into
+ * `block`-token blocks from token 0.  A block stands for the centre of its
+ * valid tokens (token t covers [t, t+1)); the segment holding that centre is
+ * mapped by relative position onto the same segment of the source scale and
+ * the source token found there, floor(start_src + (c - start_dst) *
+ * len_src / len_dst), names the source block (the pages give no mapping;
+ * this is the plain reading of "the same place at the other scale").
+ *   S_src [B,H,ceil(src_n_cur/block), ceil(src_n/block)] float32,
+ *   S_dst [B,H,ceil(dst_n_cur/block), ceil(dst_n/block)] float32,
+ *   src_n = src_n_text + src_n_ref + src_n_cur (likewise dst_n); device
+ *   memory, caller-owned, not overlapping.  S_dst is fully overwritten.
+ * Errors (nothing written): INVALID_ARGUMENT for null pointers, B or H < 1,
+ * negative segment lengths, n_cur < 1, a non-empty target segment whose
+ * source segment is empty, a scale of 2^30 tokens or more, or sizes whose
+ * element count per head exceeds int32; UNSUPPORTED for block not in
+ * {32, 64, 128}.
+ */
+sparstar_status sparstar_transfer_scores(const float* S_src, int64_t B, int64_t H, int64_t block,
+                                         int64_t src_n_text, int64_t src_n_ref, int64_t src_n_cur,
+                                         int64_t dst_n_text, int64_t dst_n_ref, int64_t dst_n_cur,
+                                         float* S_dst, void* stream);
+
 /* Host-only helpers (no HIP call, no error state). */
 /* ceil(n_forced_tokens / block): leading blocks that hold forced tokens; -1 on bad input. */
 int64_t sparstar_forced_blocks(int64_t n_forced_tokens, int64_t block);

@@ -268,8 +268,8 @@ def token_topk_bound_rows(q, k, n_forced_blocks, k_blocks, rows, block=128, scal
 # Mask reuse -- the ablation baseline the method is compared against
 # ([R] "Extended reading notes", "Core claim": a block selection carried over
 # from another scale, or across a clip boundary, keeps less attention mass
-# than a fresh one; [A] "Abstract (arXiv)": recomputing the selection at each
-# target scale against reusing a transferred mask).
+# than a fresh one; [A] "Abstract (arXiv)": the paper's analyses compare a
+# selection computed anew per scale with one carried over).
 #
 # The pages do not say how block indices map between scales.  Reading: a
 # scale's geometry is (n_text, n_ref, n_cur); queries are the current scale

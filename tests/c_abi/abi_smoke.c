@@ -73,6 +73,8 @@ int main(void) {
   CHECK(hipMalloc((void**)&qbar, B * H * nqb * D * 4) == hipSuccess);
   CHECK(hipMalloc((void**)&kbar, B * H * nkb * D * 4) == hipSuccess);
   CHECK(hipMalloc((void**)&S, B * H * nqb * nkb * 4) == hipSuccess);
+  float* S2;
+  CHECK(hipMalloc((void**)&S2, B * H * nqb * nkb * 4) == hipSuccess);
   CHECK(hipMalloc((void**)&cnt, B * H * nqb * 4) == hipSuccess);
   CHECK(hipMalloc((void**)&idx, B * H * nqb * kept * 4) == hipSuccess);
   CHECK(hipMalloc((void**)&dcnt, B * H * nqb * 4) == hipSuccess);
@@ -95,6 +97,8 @@ int main(void) {
   CHECK(sparstar_block_sparse_attn_fwd(q, k, v, SPARSTAR_BF16, B, H, Nq, Nk, D, blk, dcnt, didx,
                                        nkb, tau, o, lse_d, NULL) == SPARSTAR_OK);
   CHECK(sparstar_retained_mass(lse, lse_d, B * H * Nq, mass, NULL) == SPARSTAR_OK);
+  /* the same geometry on both sides: the transferred scores are the scores */
+  CHECK(sparstar_transfer_scores(S, B, H, blk, 130, 270, Nq, 130, 270, Nq, S2, NULL) == SPARSTAR_OK);
   /* a rejected call enqueues nothing and explains itself */
   CHECK(sparstar_block_means(q, SPARSTAR_BF16, B, H, Nq, 96, blk, qbar, NULL) ==
         SPARSTAR_ERR_UNSUPPORTED);
@@ -116,6 +120,11 @@ int main(void) {
     CHECK(hi[r * kept + kept - 1] < nkb);
   }
   for (int64_t t = 0; t < B * H * Nq; ++t) CHECK(hm[t] > 0.f && hm[t] <= 1.f);
+  float* hs = malloc(B * H * nqb * nkb * 4);
+  float* hs2 = malloc(B * H * nqb * nkb * 4);
+  CHECK(hipMemcpy(hs, S, B * H * nqb * nkb * 4, hipMemcpyDeviceToHost) == hipSuccess);
+  CHECK(hipMemcpy(hs2, S2, B * H * nqb * nkb * 4, hipMemcpyDeviceToHost) == hipSuccess);
+  CHECK(memcmp(hs, hs2, B * H * nqb * nkb * 4) == 0);
   for (size_t i = 0; i < nq; ++i) CHECK(isfinite(from_bf16(ho[i])) && fabsf(from_bf16(ho[i])) <= 1.f);
   printf("abi_smoke ok\n");
   return 0;

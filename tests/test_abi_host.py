@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_helpers():
-    assert sp.version() == 10000
+    assert sp.version() == 10100
     assert sp.forced_blocks(0) == 0
     assert sp.forced_blocks(1) == 1
     assert sp.forced_blocks(128) == 1
@@ -141,6 +141,35 @@ def test_retained_mass_validation():
     _err(f(NULL, FAKE, 10, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "null")
     _err(f(FAKE, FAKE, 10, NULL, NULL), sp.ERR_INVALID_ARGUMENT, "null")
     assert f(NULL, NULL, 0, NULL, NULL) == sp.OK   # nothing to do, nothing touched
+
+
+def test_transfer_validation():
+    f = _lib().sparstar_transfer_scores
+    FAKE2 = ctypes.c_void_p(8192)
+    args = [FAKE, 1, 16, 128, 512, 32000, 32000, 512, 72000, 72000, FAKE2, NULL]
+
+    def call(**kw):
+        a = list(args)
+        pos = {"src": 0, "B": 1, "H": 2, "block": 3, "st": 4, "sr": 5, "sc": 6, "dt": 7, "dr": 8,
+               "dc": 9, "dst": 10}
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    _err(call(src=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(dst=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(dst=FAKE), sp.ERR_INVALID_ARGUMENT, "overlap")
+    _err(call(B=0), sp.ERR_INVALID_ARGUMENT, "B and H")
+    _err(call(block=256), sp.ERR_UNSUPPORTED, "block")
+    _err(call(block=96), sp.ERR_UNSUPPORTED, "block")
+    _err(call(sr=-1), sp.ERR_INVALID_ARGUMENT, ">= 0")
+    _err(call(sr=0), sp.ERR_INVALID_ARGUMENT, "empty source segment")
+    _err(call(st=0), sp.ERR_INVALID_ARGUMENT, "empty source segment")
+    _err(call(sc=0), sp.ERR_INVALID_ARGUMENT, "empty source segment")
+    _err(call(sc=0, dc=0, st=1, sr=1), sp.ERR_INVALID_ARGUMENT, "n_cur")
+    _err(call(dr=1 << 30), sp.ERR_INVALID_ARGUMENT, "2^30")
+    _err(call(dr=600_000_000, dc=600_000_000), sp.ERR_INVALID_ARGUMENT, "2^30")
+    _err(call(block=32, dr=400_000_000, dc=400_000_000), sp.ERR_INVALID_ARGUMENT, "int32")
 
 
 def test_attn_validation():
