@@ -99,6 +99,28 @@ __device__ __forceinline__ int chunk_swizzle(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);                // 8 chunks, 2 rows per 256 B
 }
 
+// Scheduling of an MFMA chain fed from LDS: N MFMAs, each consuming DSPER
+// LDS reads, with the reads kept AHEAD MFMAs in front (instruction-group
+// barriers: 0x100 = LDS reads, 0x008 = MFMAs).  Left to itself the compiler
+// issues the K reads only one or two MFMAs ahead, so each MFMA waits for
+// the LDS latency; reading further ahead costs a few registers and removes
+// most of those waits (the arithmetic and its order are unchanged).
+template <int R, int DSPER>
+__device__ __forceinline__ void mfma_ds_interleave() {
+  if constexpr (R > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, DSPER, 0);
+    mfma_ds_interleave<R - 1, DSPER>();
+  }
+}
+template <int AHEAD, int N, int DSPER>
+__device__ __forceinline__ void schedule_mfma_chain() {
+  constexpr int A = AHEAD < N ? AHEAD : N;
+  __builtin_amdgcn_sched_group_barrier(0x100, A * DSPER, 0);
+  mfma_ds_interleave<N - A, DSPER>();
+  __builtin_amdgcn_sched_group_barrier(0x008, A, 0);
+}
+
 template <int D, int kBlock>
 __global__ __launch_bounds__(64 * (kBlock / 32), SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -281,6 +303,7 @@ __global__ __launch_bounds__(64 * (kBlock / 32), SPARSTAR_ATTN_WAVES_PER_EU) voi
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + 32 * kt * ROWB + koff[ks]);
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], sacc[kt], 0, 0, 0);
       }
+    schedule_mfma_chain<4, KSTEPS * KT, 1>();   // K reads four MFMAs ahead
     // sacc[kt][r] = S(key 32*kt + (r%4) + 8*(r/4) + 4*h, query n)
     if (nv < kBK) {
 #pragma unroll
@@ -350,6 +373,7 @@ __global__ __launch_bounds__(64 * (kBlock / 32), SPARSTAR_ATTN_WAVES_PER_EU) voi
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
       }
     }
+    schedule_mfma_chain<6, NC * DT, 2>();       // V^T reads six MFMAs ahead
   };
 
   if (T > 0) fetch_tile(0, ldsK0, ldsV0);
