@@ -34,6 +34,9 @@
 //    permuted to match the score layout), and V^T is read from the natural
 //    [key][d] LDS tile with ds_read_b64_tr_b16, gfx950's transposing LDS
 //    load, using the same key permutation.
+//  * The LDS operand reads of both MFMA chains are issued several MFMAs
+//    ahead of their use (instruction-group barriers; left alone the compiler
+//    reads just in time and every MFMA waits out the LDS latency).
 //  * Vector work per score is kept to one FMA, one exp2, half a bf16 pack
 //    and half a v_dot2 (the row sum is taken over the packed bf16 weights the
 //    MFMA consumes).  The reference max is set on the first tile and only
