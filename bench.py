@@ -132,9 +132,9 @@ def cpu_baseline(x, w, kept_F, budget_s):
 
 
 def mass_diagnostic(sp, torch, x, w, q, k, v, cnt, idx, F, kept, sample_blocks=4):
-    """Retained attention mass of the selection (GPU, every query), and on a
-    sample of query blocks of head 0 the oracle's mass and its token-wise
-    Top-K bound at the same budget."""
+    """Retained attention mass of the selection and its token-wise Top-K
+    bound at the same budget (GPU, every query; bf16 inputs), and on a sample
+    of query blocks of head 0 the oracle's mass and bound beside them."""
     import oracle
     mass = sp.selection_retained_mass(q, k, v, cnt, idx)
     torch.cuda.synchronize()
@@ -152,7 +152,7 @@ def mass_diagnostic(sp, torch, x, w, q, k, v, cnt, idx, F, kept, sample_blocks=4
     ub_all = np.concatenate([ub[r] for r in rows])
     gm = mass[0, 0].float().cpu().numpy()
     g_rows = np.concatenate([gm[i * 128:i * 128 + om[(0, 0, i)].size] for (_, _, i) in rows])
-    return {
+    out = {
         "retained_mass_mean": round(float(m.mean()), 5),
         "retained_mass_p05": round(float(np.quantile(m, 0.05)), 5),
         "retained_mass_min": round(float(m.min()), 5),
@@ -162,6 +162,22 @@ def mass_diagnostic(sp, torch, x, w, q, k, v, cnt, idx, F, kept, sample_blocks=4
         "sample_token_topk_bound": round(float(ub_all.mean()), 5),
         "sample_mass_over_bound": round(float(om_all.mean() / ub_all.mean()), 5),
     }
+    if w.dtype == "bf16":
+        # the token-wise bound for every query on the GPU (the sample checks it)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        bound = sp.token_topk_bound(q, k, F, kept - F)
+        ev[1].record()
+        torch.cuda.synchronize()
+        b_np = bound.float().cpu().numpy()
+        gb_rows = np.concatenate([b_np[0, 0, i * 128:i * 128 + ub[(0, 0, i)].size] for (_, _, i) in rows])
+        out.update({
+            "sample_bound_gpu_max_abs_diff": float(np.abs(gb_rows - ub_all).max()),
+            "token_topk_bound_mean": round(float(b_np.mean()), 5),
+            "mass_over_bound": round(float(m.mean() / b_np.mean()), 5),
+            "token_topk_bound_ms": round(ev[0].elapsed_time(ev[1]), 1),
+        })
+    return out
 
 
 def mask_reuse_diagnostic(sp, torch, w, q, k, v, F, kept, fresh_cnt, fresh_idx):

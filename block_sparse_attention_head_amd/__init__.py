@@ -10,4 +10,5 @@ from .binding import (  # noqa: F401
     SparstarError, block_means, block_scores, block_sparse_attn_fwd, forced_blocks,
     kept_blocks, last_error, lib, select_blocks, select_blocks_from_means, sparse_attention, version,
     retained_mass, selection_retained_mass, transfer_scores, transferred_selection,
+    token_topk_bound,
 )

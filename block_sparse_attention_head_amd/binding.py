@@ -26,6 +26,8 @@ _SIGNATURES = {
     "sparstar_block_sparse_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64,
                                                       _i64, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
     "sparstar_retained_mass": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp]),
+    "sparstar_token_topk_bound": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                                 _i64, _i64, _i64, _f32, _vp, _vp]),
     "sparstar_transfer_scores": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                                 _i64, _vp, _vp]),
     "sparstar_forced_blocks": (_i64, [_i64, _i64]),
@@ -205,6 +207,23 @@ def retained_mass(lse_sel, lse_dense, out=None, stream=None):
         out = torch.empty_like(lse_sel)
     _check(lib().sparstar_retained_mass(_dev(lse_sel, "lse_sel"), _dev(lse_dense, "lse_dense"),
                                         lse_sel.numel(), _dev(out, "mass"), _stream(stream)))
+    return out
+
+
+def token_topk_bound(q, k, n_forced_blocks, k_blocks, block=BLOCK, scale=None, out=None,
+                     stream=None):
+    """Token-wise Top-K upper bound of the retained mass per query token
+    [B,H,Nq] at the budget of n_forced_blocks forced + k_blocks ranked blocks."""
+    torch = _torch()
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _check(lib().sparstar_token_topk_bound(_dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, Nq, Nk, D,
+                                           block, n_forced_blocks, k_blocks, scale, _dev(out, "bound"),
+                                           _stream(stream)))
     return out
 
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libsparstar.so")
 SOURCES = ["api.hip", "block_means.hip", "block_scores.hip", "select_blocks.hip",
            "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "retained_mass.hip",
-           "transfer_scores.hip"]
+           "transfer_scores.hip", "token_bound.hip"]
 ARCH = "gfx950"
 
 

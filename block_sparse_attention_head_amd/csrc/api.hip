@@ -76,7 +76,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" {
 
-int32_t sparstar_version(void) { return 10100; }
+int32_t sparstar_version(void) { return 10200; }
 
 const char* sparstar_last_error(void) { return g_err; }
 
@@ -225,6 +225,34 @@ sparstar_status sparstar_transfer_scores(const float* S_src, int64_t B, int64_t 
     return invalid(fn, "nqb*nkb per head must fit in int32");
   return launch_transfer_scores(S_src, B * H, block, src, dst, S_dst,
                                 static_cast<hipStream_t>(stream));
+}
+
+sparstar_status sparstar_token_topk_bound(const void* q, const void* k, sparstar_dtype dtype,
+                                          int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                                          int64_t block, int64_t n_forced_blocks, int64_t k_blocks,
+                                          float scale, float* bound, void* stream) {
+  const char* fn = "sparstar_token_topk_bound";
+  clear_error();
+  if (!q || !k || !bound) return invalid(fn, "null pointer");
+  if (dtype != SPARSTAR_BF16 && dtype != SPARSTAR_FP32) return invalid(fn, "unknown dtype");
+  if (dtype != SPARSTAR_BF16) return unsupported(fn, "only bf16 inputs are supported");
+  if (!aligned16(q) || !aligned16(k)) return invalid(fn, "q and k must be 16-byte aligned");
+  if (Nq < 1 || Nk < 1) return invalid(fn, "sequence lengths must be >= 1");
+  sparstar_status st = check_bhnd(fn, B, H, Nq > Nk ? Nq : Nk, D);
+  if (st != SPARSTAR_OK) return st;
+  if ((st = check_block(fn, block)) != SPARSTAR_OK) return st;
+  if (n_forced_blocks < 0 || k_blocks < 0) return invalid(fn, "block counts must be >= 0");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return invalid(fn, "scale must be finite and > 0");
+  // token budget of the block policy (counts clamped to nkb first, so the
+  // products stay small)
+  const int64_t nkb = (Nk + block - 1) / block;
+  const int64_t fb = n_forced_blocks < nkb ? n_forced_blocks : nkb;
+  const int64_t kb = k_blocks < nkb ? k_blocks : nkb;
+  const int64_t f_tok = fb * block < Nk ? fb * block : Nk;
+  const int64_t m_tok = kb * block < Nk - f_tok ? kb * block : Nk - f_tok;
+  return launch_token_topk_bound(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                 B * H, Nq, Nk, D, f_tok, m_tok, scale, bound,
+                                 static_cast<hipStream_t>(stream));
 }
 
 sparstar_status sparstar_block_sparse_attn_fwd(const void* q, const void* k, const void* v,

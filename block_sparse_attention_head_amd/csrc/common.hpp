@@ -50,6 +50,10 @@ sparstar_status launch_transfer_scores(const float* S_src, int64_t BH, int64_t b
                                        const int64_t src_geom[3], const int64_t dst_geom[3],
                                        float* S_dst, hipStream_t s);
 
+sparstar_status launch_token_topk_bound(const uint16_t* q, const uint16_t* k, int64_t BH, int64_t Nq,
+                                        int64_t Nk, int64_t D, int64_t f_tok, int64_t m_tok,
+                                        float scale, float* bound, hipStream_t s);
+
 sparstar_status check_launch(const char* what);
 
 // ---------------------------------------------------------------------------

@@ -1,0 +1,265 @@
+// Token-wise Top-K upper bound of the retained attention mass (SparSTAR
+// review, "Core claim": fresh block-wise Top-K is judged against the
+// token-wise Top-K upper bound at the same budget).
+//
+// For every query token t, with p_s the dense softmax probability of key s:
+//   bound[t] = sum of p_s over the forced keys s < f_tok
+//            + sum of the m_tok largest p_s over the other keys,
+// f_tok = min(F * block, Nk) and m_tok = min(k * block, Nk - f_tok) for F
+// forced and k ranked blocks: the mass the best token-wise selection of the
+// same size keeps, which bounds the block selection's mass from above.
+//
+// Design: one workgroup of 4 waves x 32 queries per (b*h, 128 queries),
+// streaming every K tile of the head through a two-slot LDS ring (the same
+// direct-to-LDS loads, swizzle and S^T = K Q^T MFMA tiles as the attention
+// kernel) several times:
+//   pass 0     running max M, Z = sum 2^(l - M), the forced part, and the
+//              range [lo, hi] of the other keys' logits l (log2 units);
+//   passes 1-P each splits [lo, hi] at kThr evenly spaced thresholds and
+//              counts the eligible logits above each, keeping the piece that
+//              holds the m_tok-th largest (count above hi < m_tok <= count
+//              at or above lo);
+//   last pass  sum of 2^(l - M) over the eligible logits above hi and their
+//              count c; the remaining m_tok - c keys lie in [lo, hi] and are
+//              counted at 2^(hi - M), so the result is an upper bound within
+//              a factor 2^(hi - lo) of the exact value on those keys
+//              (hi - lo is the logit range / (kThr + 1)^P: 8^7 ~ 2.1e6).
+// Lanes l and l^32 hold the same query (half the keys each); their partial
+// sums and counts are combined after every pass.
+#include <cmath>
+
+#include "tile_common.hpp"
+
+namespace sparstar {
+namespace {
+
+constexpr int kThr = 7;       // thresholds per bisection pass
+constexpr int kPasses = 7;    // bisection passes
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void token_bound_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int Nq, int Nk, int nqb, int BH,
+    int f_tok, int m_tok, float sl2, float* __restrict__ bound) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int kBlock = 128, kBK = 64;
+  constexpr int ROWB = 2 * D;
+  constexpr int CPR = D / 8;
+  constexpr int TILEB = kBK * ROWB;
+  constexpr int RPI = 1024 / ROWB;
+  constexpr int DPW = TILEB / 1024 / 4;
+  constexpr int KT = kBK / 32;
+  constexpr int KSTEPS = D / 16;
+  __shared__ __attribute__((aligned(1024))) char ldsK0[TILEB];
+  __shared__ __attribute__((aligned(1024))) char ldsK1[TILEB];
+
+  int64_t bh;
+  int i;
+  {
+    const int p = blockIdx.x;
+    const int run = (nqb + kXcds - 1) / kXcds;
+    const int per_head = run * kXcds;
+    const int head = p / per_head;
+    const int r = p - head * per_head;
+    i = (r % kXcds) * run + r / kXcds;
+    bh = head;
+    if (i >= nqb || head >= BH) return;   // padding launches (whole workgroup)
+  }
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int l = tid % 64, h = l / 32, n = l % 32;
+  const int tok = i * kBlock + 32 * w + n;
+  const bool qvalid = tok < Nq;
+
+  bf16x8 qop[KSTEPS];
+  {
+    const uint16_t* qp = q + (bh * Nq + (qvalid ? tok : 0)) * static_cast<int64_t>(D) + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 x = qvalid ? *reinterpret_cast<const u32x4*>(qp + 16 * ks) : u32x4{0, 0, 0, 0};
+      qop[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  const uint32_t head_bytes = static_cast<uint32_t>(Nk) * ROWB;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(k + bh * static_cast<int64_t>(Nk) * D), 0, head_bytes, kBufferRsrcWord3);
+  const int T = (Nk + kBK - 1) / kBK;
+  const int dma_row0 = RPI * w + l / CPR;
+  const int dma_col = 16 * ((l % CPR) ^ chunk_swizzle<D>(dma_row0));
+  const int dma_off0 = dma_row0 * ROWB + dma_col;
+  // tile t = keys [64 t, 64 t + 64); rows past Nk re-read row Nk - 1 (finite, masked)
+  auto fetch_tile = [&](int t, char* dst) {
+    const int key0 = t * kBK;
+    if (key0 + kBK <= Nk) {
+#pragma unroll
+      for (int m = 0; m < DPW; ++m)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + 1024 * (4 * m + w)), 16,
+                                                 dma_off0 + 4096 * m, key0 * ROWB, 0, 0);
+    } else {
+#pragma unroll
+      for (int m = 0; m < DPW; ++m) {
+        const int rr = min(key0 + dma_row0 + 4 * RPI * m, Nk - 1);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + 1024 * (4 * m + w)), 16,
+                                                 rr * ROWB + dma_col, 0, 0, 0);
+      }
+    }
+  };
+  int koff[KSTEPS];
+  {
+    const int sw = chunk_swizzle<D>(n);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) koff[ks] = n * ROWB + 16 * ((2 * ks + h) ^ sw);
+  }
+
+  // One sweep over every key tile: visit(l, key) for the 32 logits (log2
+  // units) of this lane in each tile, keys in [0, Nk) only.
+  auto sweep = [&](auto&& visit) {
+    fetch_tile(0, ldsK0);
+    auto tile = [&](int t, const char* Kl, char* Kn) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (t + 1 < T) fetch_tile(t + 1, Kn);
+      f32x16 sacc[KT];
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kt][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kl + 32 * kt * ROWB + koff[ks]);
+          sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], sacc[kt], 0, 0, 0);
+        }
+      schedule_mfma_chain<4, KSTEPS * KT, 1>();
+      // sacc[kt][r] = S(key 32 kt + (r % 4) + 8 (r / 4) + 4 h of the tile, query n)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = t * kBK + 32 * kt + (r % 4) + 8 * (r / 4) + 4 * h;
+          if (key < Nk) visit(sacc[kt][r] * sl2, key);
+        }
+    };
+    for (int t = 0; t < T; t += 2) {
+      tile(t, ldsK0, ldsK1);
+      if (t + 1 < T) tile(t + 1, ldsK1, ldsK0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // every wave is done with both slots before the next sweep
+  };
+
+  // ---- pass 0: max, normaliser, forced mass, range of the other logits ----
+  float M = -INFINITY, Z = 0.f, Fs = 0.f, lo = INFINITY, hi = -INFINITY;
+  sweep([&](float x, int key) {
+    if (x > M) {                         // rescale the running sums to the new max
+      const float a = __builtin_amdgcn_exp2f(M - x);
+      Z *= a;
+      Fs *= a;
+      M = x;
+    }
+    const float e = __builtin_amdgcn_exp2f(x - M);
+    Z += e;
+    if (key < f_tok) {
+      Fs += e;
+    } else {
+      lo = fminf(lo, x);
+      hi = fmaxf(hi, x);
+    }
+  });
+  {
+    const float Mp = partner_lane32(M);
+    const float Mq = fmaxf(M, Mp);
+    const float a = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mq);
+    const float Zs = Z * a, Fss = Fs * a;
+    Z = Zs + partner_lane32(Zs);
+    Fs = Fss + partner_lane32(Fss);
+    M = Mq;
+    lo = fminf(lo, partner_lane32(lo));
+    hi = fmaxf(hi, partner_lane32(hi));
+  }
+  const int n_elig = Nk - f_tok;
+
+  // ---- bisection passes: keep [lo, hi] with #(> hi) < m_tok <= #(>= lo) ----
+  if (m_tok > 0 && m_tok < n_elig) {
+    for (int pass = 0; pass < kPasses; ++pass) {
+      float thr[kThr];
+      const float step = (hi - lo) / static_cast<float>(kThr + 1);
+#pragma unroll
+      for (int j = 0; j < kThr; ++j) thr[j] = lo + step * static_cast<float>(j + 1);
+      int cnt[kThr];
+#pragma unroll
+      for (int j = 0; j < kThr; ++j) cnt[j] = 0;
+      sweep([&](float x, int key) {
+        if (key >= f_tok) {
+#pragma unroll
+          for (int j = 0; j < kThr; ++j) cnt[j] += x > thr[j] ? 1 : 0;
+        }
+      });
+      // counts are non-increasing in j: the first threshold with fewer than
+      // m_tok logits above it becomes hi, the one before it lo
+      float nlo = lo, nhi = hi;
+      bool found = false;
+#pragma unroll
+      for (int j = 0; j < kThr; ++j) {
+        const int c = cnt[j] + __float_as_int(partner_lane32(__int_as_float(cnt[j])));
+        if (!found && c < m_tok) {
+          nhi = thr[j];
+          found = true;
+        }
+        if (!found) nlo = thr[j];
+      }
+      lo = nlo;
+      hi = nhi;
+    }
+  }
+
+  // ---- last pass: the eligible mass above hi and its count ----
+  float Sa = 0.f;
+  int ca = 0;
+  if (m_tok > 0 && m_tok < n_elig) {
+    sweep([&](float x, int key) {
+      if (key >= f_tok && x > hi) {
+        Sa += __builtin_amdgcn_exp2f(x - M);
+        ++ca;
+      }
+    });
+    Sa += partner_lane32(Sa);
+    ca += __float_as_int(partner_lane32(__int_as_float(ca)));
+  }
+
+  if (qvalid && h == 0) {
+    float b;
+    if (m_tok >= n_elig) b = 1.f;                       // every key kept
+    else if (m_tok <= 0) b = Z > 0.f ? Fs / Z : 0.f;    // forced keys only
+    else b = (Fs + Sa + static_cast<float>(m_tok - ca) * __builtin_amdgcn_exp2f(hi - M)) / Z;
+    bound[bh * Nq + tok] = fminf(b, 1.f);
+  }
+#endif
+}
+
+template <int D>
+sparstar_status launch_d(const uint16_t* q, const uint16_t* k, int64_t BH, int64_t Nq, int64_t Nk,
+                         int64_t f_tok, int64_t m_tok, float scale, float* bound, hipStream_t s) {
+  const int64_t nqb = (Nq + 127) / 128;
+  const int64_t launches = BH * ((nqb + kXcds - 1) / kXcds) * kXcds;
+  if (launches > 2147483647LL) {
+    set_error("sparstar_token_topk_bound: grid too large");
+    return SPARSTAR_ERR_INVALID_ARGUMENT;
+  }
+  token_bound_kernel<D><<<dim3(static_cast<uint32_t>(launches)), dim3(256), 0, s>>>(
+      q, k, (int)Nq, (int)Nk, (int)nqb, (int)BH, (int)f_tok, (int)m_tok,
+      scale * 1.4426950408889634f, bound);
+  return check_launch("sparstar_token_topk_bound");
+}
+
+}  // namespace
+
+sparstar_status launch_token_topk_bound(const uint16_t* q, const uint16_t* k, int64_t BH, int64_t Nq,
+                                        int64_t Nk, int64_t D, int64_t f_tok, int64_t m_tok,
+                                        float scale, float* bound, hipStream_t s) {
+  return D == 128 ? launch_d<128>(q, k, BH, Nq, Nk, f_tok, m_tok, scale, bound, s)
+                  : launch_d<64>(q, k, BH, Nq, Nk, f_tok, m_tok, scale, bound, s);
+}
+
+}  // namespace sparstar

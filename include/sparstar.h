@@ -169,6 +169,31 @@ sparstar_status sparstar_retained_mass(const float* lse_sel, const float* lse_de
                                        float* mass, void* stream);
 
 /*
+ * Token-wise Top-K upper bound of the retained attention mass (review, "Core
+ * claim": block-wise Top-K is measured against the token-wise Top-K upper
+ * bound at the same budget).  For every query token t, with p_s the dense
+ * softmax probability of key s (scale * q_t . k_s over all Nk keys):
+ *   bound[t] = sum of p_s over s < f_tok + sum of the m_tok largest p_s over
+ *              s >= f_tok,
+ * f_tok = min(n_forced_blocks * block, Nk), m_tok = min(k_blocks * block,
+ * Nk - f_tok): the mass kept by the best selection of single keys with as
+ * many keys as n_forced_blocks forced and k_blocks ranked blocks hold.  The
+ * m_tok-th largest logit is located by bisection to within 1/2^21 of the
+ * logit range; the keys inside that last interval are counted at its upper
+ * end, so the result errs upwards only, by a relative amount below
+ * 2^(range / 2^21) - 1.  Logits are computed with bf16 MFMA and float32
+ * accumulation, sums in float32.
+ *   q [B,H,Nq,D], k [B,H,Nk,D] bf16 (16-byte aligned); bound [B,H,Nq] float32.
+ * Requires bf16 (float32 returns UNSUPPORTED), D in {64, 128}, block in
+ * {32, 64, 128}, scale finite and > 0; counts are clamped to nkb.  Runs the
+ * key stream of each head several times: a diagnostic, not a hot-path call.
+ */
+sparstar_status sparstar_token_topk_bound(const void* q, const void* k, sparstar_dtype dtype,
+                                          int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t D,
+                                          int64_t block, int64_t n_forced_blocks, int64_t k_blocks,
+                                          float scale, float* bound, void* stream);
+
+/*
  * Mask reuse, the baseline the method argues against (review, "Extended
  * reading notes" / "Core claim": a selection carried over from another scale
  * or across a clip boundary keeps less attention mass than a fresh one;

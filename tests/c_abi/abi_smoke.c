@@ -82,6 +82,8 @@ int main(void) {
   CHECK(hipMalloc((void**)&lse, B * H * Nq * 4) == hipSuccess);
   CHECK(hipMalloc((void**)&lse_d, B * H * Nq * 4) == hipSuccess);
   CHECK(hipMalloc((void**)&mass, B * H * Nq * 4) == hipSuccess);
+  float* bnd;
+  CHECK(hipMalloc((void**)&bnd, B * H * Nq * 4) == hipSuccess);
   CHECK(hipMemcpy(q, hq, nq * 2, hipMemcpyHostToDevice) == hipSuccess);
   CHECK(hipMemcpy(k, hk, nk * 2, hipMemcpyHostToDevice) == hipSuccess);
   CHECK(hipMemcpy(v, hv, nk * 2, hipMemcpyHostToDevice) == hipSuccess);
@@ -97,6 +99,8 @@ int main(void) {
   CHECK(sparstar_block_sparse_attn_fwd(q, k, v, SPARSTAR_BF16, B, H, Nq, Nk, D, blk, dcnt, didx,
                                        nkb, tau, o, lse_d, NULL) == SPARSTAR_OK);
   CHECK(sparstar_retained_mass(lse, lse_d, B * H * Nq, mass, NULL) == SPARSTAR_OK);
+  CHECK(sparstar_token_topk_bound(q, k, SPARSTAR_BF16, B, H, Nq, Nk, D, blk, F, kept - F, tau, bnd,
+                                  NULL) == SPARSTAR_OK);
   /* the same geometry on both sides: the transferred scores are the scores */
   CHECK(sparstar_transfer_scores(S, B, H, blk, 130, 270, Nq, 130, 270, Nq, S2, NULL) == SPARSTAR_OK);
   /* a rejected call enqueues nothing and explains itself */
@@ -120,6 +124,10 @@ int main(void) {
     CHECK(hi[r * kept + kept - 1] < nkb);
   }
   for (int64_t t = 0; t < B * H * Nq; ++t) CHECK(hm[t] > 0.f && hm[t] <= 1.f);
+  float* hb = malloc(B * H * Nq * 4);
+  CHECK(hipMemcpy(hb, bnd, B * H * Nq * 4, hipMemcpyDeviceToHost) == hipSuccess);
+  /* the token-wise bound at the same budget is at least the block selection's mass */
+  for (int64_t t = 0; t < B * H * Nq; ++t) CHECK(hb[t] >= hm[t] - 1e-5f && hb[t] <= 1.f);
   float* hs = malloc(B * H * nqb * nkb * 4);
   float* hs2 = malloc(B * H * nqb * nkb * 4);
   CHECK(hipMemcpy(hs, S, B * H * nqb * nkb * 4, hipMemcpyDeviceToHost) == hipSuccess);

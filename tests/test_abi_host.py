@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_helpers():
-    assert sp.version() == 10100
+    assert sp.version() == 10200
     assert sp.forced_blocks(0) == 0
     assert sp.forced_blocks(1) == 1
     assert sp.forced_blocks(128) == 1
@@ -141,6 +141,32 @@ def test_retained_mass_validation():
     _err(f(NULL, FAKE, 10, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "null")
     _err(f(FAKE, FAKE, 10, NULL, NULL), sp.ERR_INVALID_ARGUMENT, "null")
     assert f(NULL, NULL, 0, NULL, NULL) == sp.OK   # nothing to do, nothing touched
+
+
+def test_token_bound_validation():
+    f = _lib().sparstar_token_topk_bound
+    args = [FAKE, FAKE, 1, 1, 2, 300, 700, 128, 128, 2, 1, 0.088, FAKE, NULL]
+
+    def call(**kw):
+        a = list(args)
+        pos = {"q": 0, "k": 1, "dtype": 2, "B": 3, "Nq": 5, "Nk": 6, "D": 7, "block": 8, "F": 9,
+               "kb": 10, "scale": 11, "out": 12}
+        for key, v in kw.items():
+            a[pos[key]] = v
+        return f(*a)
+
+    _err(call(q=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(out=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(dtype=0), sp.ERR_UNSUPPORTED, "bf16")
+    _err(call(dtype=7), sp.ERR_INVALID_ARGUMENT, "dtype")
+    _err(call(q=ctypes.c_void_p(4100)), sp.ERR_INVALID_ARGUMENT, "aligned")
+    _err(call(Nk=0), sp.ERR_INVALID_ARGUMENT, "sequence")
+    _err(call(D=96), sp.ERR_UNSUPPORTED, "D must be")
+    _err(call(block=96), sp.ERR_UNSUPPORTED, "block")
+    _err(call(F=-1), sp.ERR_INVALID_ARGUMENT, "block counts")
+    _err(call(kb=-2), sp.ERR_INVALID_ARGUMENT, "block counts")
+    _err(call(scale=0.0), sp.ERR_INVALID_ARGUMENT, "scale")
+    _err(call(scale=float("inf")), sp.ERR_INVALID_ARGUMENT, "scale")
 
 
 def test_transfer_validation():
