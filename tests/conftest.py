@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests cannot run here; they are selected with -m gpu on the GPU machine.
+    # Without a visible GPU the GPU tests are skipped (select them with -m gpu on a GPU machine).
     import torch
     if torch.cuda.is_available():
         return
