@@ -31,7 +31,17 @@ METRIC = "selected-block attn TFLOP/s + ms per scale (score+select+attn) at 72k 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.txt")
-ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_head_amd", "csrc", "attn_fwd_bf16.hip")
+# the attention kernel's sources: counters are valid only for this exact code
+ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_head_amd", "csrc", f)
+                for f in ("attn_fwd_bf16.hip", "tile_common.hpp", "common.hpp")]
+
+
+def attn_source_sha():
+    h = hashlib.sha256()
+    for path in ATTN_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -74,8 +84,7 @@ def traffic_for_attention(workload_name):
                     continue
                 key, val = line.split(":", 1)
                 rec[key.strip()] = val.strip()
-        sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != sha or rec.get("workload") != workload_name:
+        if rec.get("source_sha256") != attn_source_sha() or rec.get("workload") != workload_name:
             return None
         return int(float(rec["hbm_bytes_per_launch"]))
     except (OSError, ValueError, KeyError):
