@@ -150,7 +150,9 @@ def select_blocks(S, n_forced_blocks, density, max_kept=None, kv_count=None, kv_
     if kv_count is None:
         kv_count = torch.empty((B, H, nqb), dtype=torch.int32, device=S.device)
     if kv_index is None:
-        kv_index = torch.empty((B, H, nqb, max(1, max_kept)), dtype=torch.int32, device=S.device)
+        # at least one column, and the library writes all of them (-1 padding)
+        max_kept = max(1, max_kept)
+        kv_index = torch.empty((B, H, nqb, max_kept), dtype=torch.int32, device=S.device)
     _check(lib().sparstar_select_blocks(_dev(S, "S"), B, H, nqb, nkb, n_forced_blocks, density,
                                         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
                                         max_kept, _stream(stream)))
@@ -172,8 +174,8 @@ def select_blocks_from_means(qbar, kbar, n_forced_blocks, density, tau=None, max
     if kv_count is None:
         kv_count = torch.empty((B, H, nqb), dtype=torch.int32, device=qbar.device)
     if kv_index is None:
-        kv_index = torch.empty((B, H, nqb, max(1, max_kept)), dtype=torch.int32,
-                               device=qbar.device)
+        max_kept = max(1, max_kept)
+        kv_index = torch.empty((B, H, nqb, max_kept), dtype=torch.int32, device=qbar.device)
     _check(lib().sparstar_select_blocks_from_means(
         _dev(qbar, "qbar"), _dev(kbar, "kbar"), B, H, nqb, nkb, D, tau, n_forced_blocks, density,
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept, _stream(stream)))
