@@ -63,3 +63,32 @@ def test_zero_budget_writes_padding():
     assert np.all(res["kv_index"].cpu().numpy() == -1)
     assert np.all(to_f64(res["o"]) == 0.0)
     assert np.all(np.isneginf(to_f64(res["lse"])))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_transfer_and_bound(seed):
+    """Random geometries for the score transfer (bit-exact) and random shapes
+    and budgets for the token-wise bound (within 1e-4)."""
+    rng = np.random.default_rng(5000 + seed)
+    block = int(rng.choice([32, 64, 128]))
+    t = int(rng.integers(0, 700))
+    src = (t, int(rng.integers(0 if rng.random() < 0.2 else 1, 3000)), int(rng.integers(1, 3000)))
+    dst = (t, int(rng.integers(0, 3000)) if src[1] > 0 else 0, int(rng.integers(1, 3000)))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+    S = rng.standard_normal((B, H, -(-src[2] // block), -(-sum(src) // block))).astype(np.float32)
+    g = sp.transfer_scores(to_dev(S, "fp32"), src, dst, block=block).cpu().numpy()
+    assert np.array_equal(g, oracle.transfer_scores(S, src, dst, block)), (src, dst, block)
+
+    D = int(rng.choice([64, 128]))
+    Nq, Nk = int(rng.integers(1, 600)), int(rng.integers(1, 2000))
+    q = bf16_bits_from_f32(rng.standard_normal((1, H, Nq, D), dtype=np.float32))
+    k = bf16_bits_from_f32(rng.standard_normal((1, H, Nk, D), dtype=np.float32) * 1.5)
+    nkb = -(-Nk // block)
+    F, kb = int(rng.integers(0, nkb + 1)), int(rng.integers(0, nkb + 1))
+    log(f"random transfer/bound {seed}: block={block} src={src} dst={dst}; D={D} Nq={Nq} Nk={Nk} F={F} k={kb}")
+    b = to_f64(sp.token_topk_bound(to_dev(q, "bf16"), to_dev(k, "bf16"), F, kb, block=block))
+    qd, kd = oracle.decode(q, "bf16"), oracle.decode(k, "bf16")
+    rows = [(0, h, i) for h in range(H) for i in range(-(-Nq // block))]
+    ref = oracle.token_topk_bound_rows(qd, kd, F, kb, rows, block=block)
+    for (bb, h, i), m in ref.items():
+        assert np.abs(b[bb, h, i * block:i * block + m.size] - m).max() <= 1e-4, (seed, h, i)
