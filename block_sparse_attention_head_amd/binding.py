@@ -112,6 +112,38 @@ def _dev(t, name):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(t, name, shape, dtype):
+    """Shape and dtype of a caller-supplied tensor, checked before any call:
+    the library reads and writes through raw pointers at these strides."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _selection_buffers(lead, n_forced_blocks, density, nkb, max_kept, kv_count, kv_index, device):
+    """kv_count [*lead] and kv_index [*lead, max_kept] int32; max_kept defaults
+    to the width of a supplied kv_index, else to the kept-block count."""
+    torch = _torch()
+    if max_kept is None:
+        if kv_index is not None:
+            max_kept = kv_index.shape[-1]
+        else:
+            max_kept = kept_blocks(nkb, n_forced_blocks, density)
+            if max_kept < 0:
+                raise SparstarError(ERR_INVALID_ARGUMENT, "invalid n_forced_blocks or density")
+    if kv_index is None:
+        # at least one column, and the library writes all of them (-1 padding)
+        max_kept = max(1, max_kept)
+    if kv_count is None:
+        kv_count = torch.empty(lead, dtype=torch.int32, device=device)
+    if kv_index is None:
+        kv_index = torch.empty((*lead, max_kept), dtype=torch.int32, device=device)
+    _expect(kv_count, "kv_count", lead, torch.int32)
+    _expect(kv_index, "kv_index", (*lead, max_kept), torch.int32)
+    return max_kept, kv_count, kv_index
+
+
 def block_means(x, block=BLOCK, out=None, stream=None):
     """x [B,H,N,D] bf16/fp32 -> [B,H,ceil(N/block),D] fp32."""
     torch = _torch()
@@ -119,6 +151,7 @@ def block_means(x, block=BLOCK, out=None, stream=None):
     nb = -(-N // block)
     if out is None:
         out = torch.empty((B, H, nb, D), dtype=torch.float32, device=x.device)
+    _expect(out, "out", (B, H, nb, D), torch.float32)
     _check(lib().sparstar_block_means(_dev(x, "x"), _dtype_code(x), B, H, N, D, block,
                                       _dev(out, "out"), _stream(stream)))
     return out
@@ -131,8 +164,11 @@ def block_scores(qbar, kbar, tau=None, out=None, stream=None):
     nkb = kbar.shape[2]
     if tau is None:
         tau = 1.0 / math.sqrt(D)
+    _expect(qbar, "qbar", (B, H, nqb, D), torch.float32)
+    _expect(kbar, "kbar", (B, H, nkb, D), torch.float32)
     if out is None:
         out = torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=qbar.device)
+    _expect(out, "S", (B, H, nqb, nkb), torch.float32)
     _check(lib().sparstar_block_scores(_dev(qbar, "qbar"), _dev(kbar, "kbar"), B, H, nqb, nkb, D,
                                        tau, _dev(out, "S"), _stream(stream)))
     return out
@@ -143,16 +179,9 @@ def select_blocks(S, n_forced_blocks, density, max_kept=None, kv_count=None, kv_
     """-> (kv_count [B,H,nqb] int32, kv_index [B,H,nqb,max_kept] int32)."""
     torch = _torch()
     B, H, nqb, nkb = S.shape
-    if max_kept is None:
-        max_kept = kept_blocks(nkb, n_forced_blocks, density)
-        if max_kept < 0:
-            raise SparstarError(ERR_INVALID_ARGUMENT, "invalid n_forced_blocks or density")
-    if kv_count is None:
-        kv_count = torch.empty((B, H, nqb), dtype=torch.int32, device=S.device)
-    if kv_index is None:
-        # at least one column, and the library writes all of them (-1 padding)
-        max_kept = max(1, max_kept)
-        kv_index = torch.empty((B, H, nqb, max_kept), dtype=torch.int32, device=S.device)
+    _expect(S, "S", S.shape, torch.float32)
+    max_kept, kv_count, kv_index = _selection_buffers((B, H, nqb), n_forced_blocks, density, nkb,
+                                                      max_kept, kv_count, kv_index, S.device)
     _check(lib().sparstar_select_blocks(_dev(S, "S"), B, H, nqb, nkb, n_forced_blocks, density,
                                         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"),
                                         max_kept, _stream(stream)))
@@ -165,17 +194,12 @@ def select_blocks_from_means(qbar, kbar, n_forced_blocks, density, tau=None, max
     torch = _torch()
     B, H, nqb, D = qbar.shape
     nkb = kbar.shape[2]
+    _expect(qbar, "qbar", (B, H, nqb, D), torch.float32)
+    _expect(kbar, "kbar", (B, H, nkb, D), torch.float32)
     if tau is None:
         tau = 1.0 / math.sqrt(D)
-    if max_kept is None:
-        max_kept = kept_blocks(nkb, n_forced_blocks, density)
-        if max_kept < 0:
-            raise SparstarError(ERR_INVALID_ARGUMENT, "invalid n_forced_blocks or density")
-    if kv_count is None:
-        kv_count = torch.empty((B, H, nqb), dtype=torch.int32, device=qbar.device)
-    if kv_index is None:
-        max_kept = max(1, max_kept)
-        kv_index = torch.empty((B, H, nqb, max_kept), dtype=torch.int32, device=qbar.device)
+    max_kept, kv_count, kv_index = _selection_buffers((B, H, nqb), n_forced_blocks, density, nkb,
+                                                      max_kept, kv_count, kv_index, qbar.device)
     _check(lib().sparstar_select_blocks_from_means(
         _dev(qbar, "qbar"), _dev(kbar, "kbar"), B, H, nqb, nkb, D, tau, n_forced_blocks, density,
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept, _stream(stream)))
@@ -188,13 +212,22 @@ def block_sparse_attn_fwd(q, k, v, kv_count, kv_index, scale=None, block=BLOCK, 
     torch = _torch()
     B, H, Nq, D = q.shape
     Nk = k.shape[2]
+    _dtype_code(q)
+    _expect(k, "k", (B, H, Nk, D), q.dtype)
+    _expect(v, "v", (B, H, Nk, D), q.dtype)
+    nqb = -(-Nq // block)
+    max_kept = kv_index.shape[-1]
+    _expect(kv_count, "kv_count", (B, H, nqb), torch.int32)
+    _expect(kv_index, "kv_index", (B, H, nqb, max_kept), torch.int32)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty_like(q)
+    _expect(out, "out", q.shape, q.dtype)
     if lse is None and return_lse:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    max_kept = kv_index.shape[-1]
+    if lse is not None:
+        _expect(lse, "lse", (B, H, Nq), torch.float32)
     _check(lib().sparstar_block_sparse_attn_fwd(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dtype_code(q), B, H, Nq, Nk, D, block,
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept, scale,

@@ -221,6 +221,11 @@ def test_attn_validation():
     _err(call(scale=float("nan")), sp.ERR_INVALID_ARGUMENT, "scale")
     _err(call(max_kept=-1), sp.ERR_INVALID_ARGUMENT, "max_kept")
     _err(call(dtype=5), sp.ERR_INVALID_ARGUMENT, "dtype")
+    # the stated per-head limit N * D < 2^31 (byte offsets inside one head's
+    # bf16 K/V slab then fit the unsigned 32-bit buffer offsets)
+    _err(call(Nk=1 << 24), sp.ERR_INVALID_ARGUMENT, "N*D")
+    _err(call(Nq=1 << 24), sp.ERR_INVALID_ARGUMENT, "N*D")
+    _err(call(Nk=1 << 25, D=64), sp.ERR_INVALID_ARGUMENT, "N*D")
 
 
 def test_error_cleared_on_next_call():
@@ -252,5 +257,52 @@ def test_launch_failure_is_reported_without_a_gpu():
     st = _lib().sparstar_block_scores(FAKE, FAKE, 1, 1, 4, 4, 128, 0.1, FAKE, NULL)
     assert st == sp.ERR_HIP, (st, sp.last_error())
     assert sp.last_error() != ""
+    # the largest key length the API admits at D = 128 passes validation
+    st = _lib().sparstar_block_sparse_attn_fwd(FAKE, FAKE, FAKE, 1, 1, 1, 256, (1 << 24) - 1, 128,
+                                               128, FAKE, FAKE, 2, 0.088, FAKE, NULL, NULL)
+    assert st == sp.ERR_HIP, (st, sp.last_error())
     _err(_lib().sparstar_block_means(NULL, 1, 1, 1, 128, 128, 128, FAKE, NULL),
          sp.ERR_INVALID_ARGUMENT, "null")
+
+
+def test_binding_checks_shapes_and_dtypes_before_calling():
+    """The binding refuses tensors whose dtype or shape does not match what
+    the library will read and write through raw pointers (host tensors here:
+    every check fails before any device pointer is taken)."""
+    import torch
+    bf, f32, i32 = torch.bfloat16, torch.float32, torch.int32
+    q = torch.zeros((1, 2, 300, 128), dtype=bf)
+    k = torch.zeros((1, 2, 500, 128), dtype=bf)
+    cnt = torch.zeros((1, 2, 3), dtype=i32)
+    idx = torch.zeros((1, 2, 3, 4), dtype=i32)
+    with pytest.raises(TypeError, match="k must be"):
+        sp.block_sparse_attn_fwd(q, k.float(), k, cnt, idx)
+    with pytest.raises(ValueError, match="v must have shape"):
+        sp.block_sparse_attn_fwd(q, k, k[:, :, :400], cnt, idx)
+    with pytest.raises(ValueError, match="k must have shape"):
+        sp.block_sparse_attn_fwd(q, k[..., :64].contiguous(), k, cnt, idx)
+    with pytest.raises(TypeError, match="kv_index must be"):
+        sp.block_sparse_attn_fwd(q, k, k, cnt, idx.long())
+    with pytest.raises(ValueError, match="kv_count must have shape"):
+        sp.block_sparse_attn_fwd(q, k, k, cnt[:, :, :2], idx)
+    with pytest.raises(ValueError, match="kv_count must have shape"):
+        sp.block_sparse_attn_fwd(q, k, k, cnt, idx, block=64)      # 5 query blocks at 64
+    with pytest.raises(ValueError, match="out must have shape"):
+        sp.block_sparse_attn_fwd(q, k, k, cnt, idx, out=q[:, :1])
+    with pytest.raises(ValueError, match="lse must have shape"):
+        sp.block_sparse_attn_fwd(q, k, k, cnt, idx, lse=torch.zeros((1, 2, 299)))
+    S = torch.zeros((1, 2, 3, 4), dtype=f32)
+    # a supplied kv_index fixes max_kept; a mismatched explicit max_kept is refused
+    with pytest.raises(ValueError, match="kv_index must have shape"):
+        sp.select_blocks(S, 1, 0.5, max_kept=3, kv_index=idx)
+    with pytest.raises(TypeError, match="S must be"):
+        sp.select_blocks(S.double(), 1, 0.5)
+    with pytest.raises(ValueError, match="kv_count must have shape"):
+        sp.select_blocks(S, 1, 0.5, kv_count=cnt[0])
+    qbar = torch.zeros((1, 2, 3, 128), dtype=f32)
+    with pytest.raises(ValueError, match="kbar must have shape"):
+        sp.select_blocks_from_means(qbar, torch.zeros((1, 1, 4, 128)), 1, 0.5)
+    with pytest.raises(ValueError, match="S must have shape"):
+        sp.block_scores(qbar, torch.zeros((1, 2, 4, 128)), out=torch.zeros((1, 2, 3, 5)))
+    with pytest.raises(ValueError, match="out must have shape"):
+        sp.block_means(q, out=torch.zeros((1, 2, 2, 128)))
