@@ -53,36 +53,18 @@
 namespace sparstar {
 namespace {
 
-// Build-time design knobs; the defaults are the measured best on MI355X
-// (64-key tiles, two waves per SIMD, XCD-aware order, default cache policy).
-#ifndef SPARSTAR_ATTN_BK
-#define SPARSTAR_ATTN_BK 64
-#endif
-#ifndef SPARSTAR_ATTN_WAVES_PER_EU
-#define SPARSTAR_ATTN_WAVES_PER_EU 2
-#endif
-#ifndef SPARSTAR_ATTN_XCD_MAP
-#define SPARSTAR_ATTN_XCD_MAP 1
-#endif
-// Keys per LDS tile: SPARSTAR_ATTN_BK (64) for 128-token blocks, 32 for the
-// smaller blocks (whose workgroups have fewer waves, so a smaller ring keeps
-// more workgroups per CU).
+// Keys per LDS tile: 64 for 128-token blocks, 32 for the smaller blocks
+// (whose workgroups have fewer waves, so a smaller ring keeps more
+// workgroups per CU).
 template <int kBlock>
-constexpr int tile_keys_of() { return kBlock >= 128 ? SPARSTAR_ATTN_BK : 32; }
+constexpr int tile_keys_of() { return kBlock >= 128 ? 64 : 32; }
 // Weights exp2(s - m_ref) may grow up to a row sum of 2^16 before the
 // reference max is moved (fp32 accumulators and bf16 weights hold that
 // range as exactly as small values).
 constexpr float kMaxRowSum = 65536.f;
-#ifndef SPARSTAR_ATTN_KV_CPOL
-#define SPARSTAR_ATTN_KV_CPOL 0   // cache-policy bits of the K/V tile loads
-#endif
-
-
-
-
 
 template <int D, int kBlock>
-__global__ __launch_bounds__(64 * (kBlock / 32), SPARSTAR_ATTN_WAVES_PER_EU) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(64 * (kBlock / 32), 2) void attn_fwd_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, int Nq, int Nk, int nqb, int BH,
     const int32_t* __restrict__ kv_count, const int32_t* __restrict__ kv_index, int max_kept,
@@ -114,11 +96,10 @@ __global__ __launch_bounds__(64 * (kBlock / 32), SPARSTAR_ATTN_WAVES_PER_EU) voi
   int64_t bh;
   int i;
   {
-    const int p = blockIdx.x;
-#if SPARSTAR_ATTN_XCD_MAP
     // Launch p runs on XCD p % 8.  Per head the query blocks are cut into 8
     // contiguous runs of `run` blocks, run x going to XCD x; consecutive
     // launches still sweep one head after another.
+    const int p = blockIdx.x;
     const int run = (nqb + kXcds - 1) / kXcds;
     const int per_head = run * kXcds;
     const int head = p / per_head;
@@ -126,10 +107,6 @@ __global__ __launch_bounds__(64 * (kBlock / 32), SPARSTAR_ATTN_WAVES_PER_EU) voi
     i = (r % kXcds) * run + r / kXcds;
     bh = head;
     if (i >= nqb || head >= BH) return;   // padding launches (whole workgroup)
-#else
-    bh = p / nqb;
-    i = p - static_cast<int>(bh) * nqb;
-#endif
   }
   const int64_t row = bh * nqb + i;
   const int tid = threadIdx.x;
@@ -198,20 +175,20 @@ __global__ __launch_bounds__(64 * (kBlock / 32), SPARSTAR_ATTN_WAVES_PER_EU) voi
       for (int m = 0; m < DPW; ++m) {
         const int u = kNW * m + w;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + 1024 * u), 16,
-                                                 dma_off[m], key0 * ROWB, 0, SPARSTAR_ATTN_KV_CPOL);
+                                                 dma_off[m], row_offset_bytes(key0, ROWB), 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + 1024 * u), 16,
-                                                 dma_off[m], key0 * ROWB, 0, SPARSTAR_ATTN_KV_CPOL);
+                                                 dma_off[m], row_offset_bytes(key0, ROWB), 0, 0);
       }
     } else {           // partial tile: rows past Nk re-read row Nk-1 (finite, masked later)
 #pragma unroll
       for (int m = 0; m < DPW; ++m) {
         const int u = kNW * m + w;
         const int rr = min(base + dma_row[m], Nk - 1);
-        const int off = rr * ROWB + (dma_off[m] - dma_row[m] * ROWB);
+        const int off = row_offset_bytes(rr, ROWB) + (dma_off[m] - dma_row[m] * ROWB);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + 1024 * u), 16,
-                                                 off, 0, 0, SPARSTAR_ATTN_KV_CPOL);
+                                                 off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + 1024 * u), 16,
-                                                 off, 0, 0, SPARSTAR_ATTN_KV_CPOL);
+                                                 off, 0, 0, 0);
       }
     }
   };
@@ -369,11 +346,7 @@ sparstar_status launch_b(const uint16_t* q, const uint16_t* k, const uint16_t* v
                          const int32_t* kv_index, int64_t max_kept, float scale, uint16_t* o,
                          float* lse, hipStream_t s) {
   const int64_t nqb = (Nq + B - 1) / B;
-#if SPARSTAR_ATTN_XCD_MAP
   const int64_t launches = BH * ((nqb + kXcds - 1) / kXcds) * kXcds;
-#else
-  const int64_t launches = BH * nqb;
-#endif
   if (launches > 2147483647LL) {
     set_error("sparstar_block_sparse_attn_fwd: grid too large");
     return SPARSTAR_ERR_INVALID_ARGUMENT;

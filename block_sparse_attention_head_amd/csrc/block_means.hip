@@ -1,6 +1,6 @@
 // Block means of Q or K over contiguous blocks of kBlock tokens (SparSTAR
-// review, "What carries the argument": block-averaged query and key vectors
-// over 128-token blocks; 32 and 64 are instantiated as well).
+// review, "What carries the argument": queries and keys are averaged per
+// block of 128 tokens; 32 and 64 are instantiated as well).
 //
 // One workgroup of 256 threads per (b*h, block): the kBlock x D slab is one
 // contiguous chunk of HBM, read once with 16-byte loads by consecutive

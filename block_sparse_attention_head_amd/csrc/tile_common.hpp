@@ -16,6 +16,15 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Byte offset of token row `row` inside one head's K or V slab, as a buffer
+// load takes it: an unsigned 32-bit value passed through an int argument.
+// The API admits N * D < 2^31 per head, so a bf16 slab holds fewer than
+// 2^32 bytes and the unsigned product cannot wrap (a signed one would from
+// row 2^31 / (2 D) on).
+__device__ __forceinline__ int row_offset_bytes(int row, int row_bytes) {
+  return static_cast<int>(static_cast<uint32_t>(row) * static_cast<uint32_t>(row_bytes));
+}
+
 __device__ __forceinline__ float partner_lane32(float x) {
   // v_permlane32_swap(x, x): lanes < 32 receive [x[l], x[l+32]], lanes >= 32
   // receive [x[l-32], x[l]]; pick the other half's value.

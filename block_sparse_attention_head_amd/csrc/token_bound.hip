@@ -94,13 +94,13 @@ __global__ __launch_bounds__(256, 2) void token_bound_kernel(
 #pragma unroll
       for (int m = 0; m < DPW; ++m)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + 1024 * (4 * m + w)), 16,
-                                                 dma_off0 + 4096 * m, key0 * ROWB, 0, 0);
+                                                 dma_off0 + 4096 * m, row_offset_bytes(key0, ROWB), 0, 0);
     } else {
 #pragma unroll
       for (int m = 0; m < DPW; ++m) {
         const int rr = min(key0 + dma_row0 + 4 * RPI * m, Nk - 1);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(dst + 1024 * (4 * m + w)), 16,
-                                                 rr * ROWB + dma_col, 0, 0, 0);
+                                                 row_offset_bytes(rr, ROWB) + dma_col, 0, 0, 0);
       }
     }
   };
