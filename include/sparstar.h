@@ -6,10 +6,10 @@
  * Attention for SpaceTime AutoRegressive Video Synthesis", pith.science, and
  * the SparSTAR abstract on mlsanity.com):
  *
- *   per (batch, head) -- "at each expensive scale and attention head"
- *   (abstract) --
- *     1. qbar_i, kbar_j: means of Q and K over contiguous 128-token blocks
- *        ("What carries the argument");
+ *   separately for every costly refinement scale and every attention head
+ *   (abstract), i.e. per (batch, head):
+ *     1. qbar_i, kbar_j: means of Q and K over runs of 128 consecutive
+ *        tokens ("What carries the argument");
  *     2. S_ij = tau * qbar_i . kbar_j with tau = D^-1/2 (Eq. 2, same section);
  *     3. keep the forced context blocks (text; for Clip 1 also the final
  *        image-pyramid reference) and jointly rank every other key block
@@ -55,16 +55,16 @@ typedef enum {
   SPARSTAR_BF16 = 1  /* bfloat16 bit patterns (uint16) */
 } sparstar_dtype;
 
-/* The pages' block size: the review's "Block size b = 128 tokens"
- * ("Assumptions & free parameters").  The means and attention entry points
+/* The pages' block size of 128 tokens (review, "Assumptions & free
+ * parameters").  The means and attention entry points
  * also take block = 64 or 32: the review notes that smaller blocks improve
  * fidelity but had no efficient kernel in the authors' environment
  * ("Assumptions & free parameters", "Referee Report" minor comment 4). */
 #define SPARSTAR_BLOCK 128
 
 /*
- * Block means ("What carries the argument": block-averaged query and key
- * vectors over contiguous 128-token blocks).
+ * Block means (review, "What carries the argument": queries and keys are
+ * averaged over runs of consecutive tokens, one run per block).
  *   x    [B,H,N,D] of `dtype`.
  *   out  [B,H,ceil(N/block),D] float32.  out[b,h,i,:] is the mean of tokens
  *        [i*block, min((i+1)*block, N)); a partial last block is divided by
@@ -130,8 +130,8 @@ sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float
                                                   void* stream);
 
 /*
- * Block-sparse forward attention ("What carries the argument": the chosen
- * blocks are executed through a forward-only path).
+ * Block-sparse forward attention (review, "What carries the argument": only
+ * the selected blocks are computed, by a forward-only operator).
  * For every query token t of query block i of (b,h):
  *   O[b,h,t,:] = sum_s softmax_s(scale * q_t . k_s) * v_s
  *   lse[b,h,t] = log sum_s exp(scale * q_t . k_s)

@@ -7,8 +7,8 @@ no code with the GPU path and must never be called from the product path.
 Sources (the pages this follows):
   [R]  "Pith review of SparSTAR: Sparse Attention for SpaceTime AutoRegressive
        Video Synthesis" (pith.science/paper/2608.10519), sections
-       "What carries the argument" (block averages over contiguous 128-token
-       blocks, S_ij = tau * qbar_i^T kbar_j with tau = D^-1/2 -- Eq. 2 --,
+       "What carries the argument" (means over blocks of 128 consecutive
+       tokens, S_ij = tau * qbar_i^T kbar_j with tau = D^-1/2 -- Eq. 2 --,
        clip-aware retention, joint ranking, forward-only execution),
        "Core claim" (fresh block-wise Top-K per scale and head),
        "Assumptions & free parameters" (density schedule, b = 128, the SSA
@@ -16,8 +16,9 @@ Sources (the pages this follows):
        -- Eq. 1).
   [A]  "SparSTAR: Sparse Attention for SpaceTime AutoRegressive Video
        Synthesis" (mlsanity.com/paper/2608.10519), "Abstract (arXiv)":
-       per scale and head, score contiguous key blocks from the current Q and
-       K, retain required conditioning context, execute selected blocks.
+       for each scale and head, rank key blocks by scores computed from that
+       scale's own Q and K, keep the conditioning context that must stay
+       visible, and compute attention over the chosen blocks only.
 
 Readings where the pages are silent (each also listed in the design notes):
   * blocks tile the whole key sequence [text | reference | current] from token
@@ -205,7 +206,8 @@ def sparse_attention(q, k, v, kv_count, kv_index, block=128, scale=None):
 # Diagnostic -- retained attention mass and the token-wise Top-K bound
 # ([R] "Core claim": block-wise Top-K recomputed per scale is compared with a
 # token-wise upper bound by the attention mass it retains; [R] "Editorial
-# extensions": the exact token-wise Top-K oracle at the same densities)
+# extensions": an exact per-token Top-K selection at equal density as the
+# reference point)
 # ---------------------------------------------------------------------------
 def _dense_probs(q_blk, k, scale):
     """Dense softmax rows p[t, s] of one query block over all Nk keys."""

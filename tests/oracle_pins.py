@@ -25,9 +25,9 @@ def _golden(name):
 
 # --- identity: block-mean dot product == average pairwise logit ------------
 def pin_identity(impl, seed=0):
-    """The review ('What carries the argument') states that the dot product of
-    block averages equals the average pairwise pre-softmax compatibility of
-    the tokens in the two blocks.  Checked by brute force over token pairs."""
+    """The review ('What carries the argument') notes that the inner product of
+    two block means is the mean, over all token pairs of the two blocks, of
+    the unscaled logit q_t . k_s.  Checked by brute force over token pairs."""
     rng = np.random.default_rng(seed)
     for D in (4, 64):
         for ni, nj in [(1, 1), (3, 1), (1, 3), (3, 64), (64, 128), (128, 128), (128, 3)]:

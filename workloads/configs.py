@@ -8,8 +8,8 @@ the final image-pyramid reference), then the current scale.  The forced
 
 Density values come from the schedule the review gives under "What carries
 the argument" and "free parameters" (0.625, 0.1875, 0.1875, 0.09375 over the
-four sparsified scales); the block size of 128 tokens is the review's
-"Block size b = 128 tokens" free parameter.  The 72,000-token final scale is
+four sparsified scales); the block size of 128 tokens is one of the
+review's free parameters.  The 72,000-token final scale is
 named in "What carries the argument".
 """
 from dataclasses import dataclass, field
