@@ -11,7 +11,10 @@ D = 128, bf16, keys = 512 text + 72,000 reference + 72,000 current, density
 Printed: one JSON line.  `value` is selected-block attention TFLOP/s over the
 whole step (selected FLOPs / ms per scale); `ms_per_step` is ms per scale
 (score + select + attn).  `roofline` is for the attention kernel (bf16 MFMA
-peak), with its duration from HIP events recorded on the launch stream.
+peak), with its duration from HIP events recorded on the launch stream.  By
+default every timed step starts with L2 and MALL cold (a 512 MiB overwrite
+before it, outside the timed region); `other_cache` holds the warm
+(back-to-back) figures, or the cold ones under --warm.
 """
 import argparse
 import hashlib
@@ -31,16 +34,20 @@ METRIC = "selected-block attn TFLOP/s + ms per scale (score+select+attn) at 72k 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.txt")
-# the attention kernel's sources: counters are valid only for this exact code
+# the attention kernel's sources and build flags: counters are valid only for
+# this exact code
 ATTN_SOURCES = [os.path.join(ROOT, "block_sparse_attention_head_amd", "csrc", f)
-                for f in ("attn_fwd_bf16.hip", "tile_common.hpp", "common.hpp")]
+                for f in ("attn_fwd_bf16.hip", "tile_common.hpp", "common.hpp")] + \
+               [os.path.join(ROOT, "include", "sparstar.h")]
 
 
 def attn_source_sha():
+    from block_sparse_attention_head_amd.build import compile_flags
     h = hashlib.sha256()
     for path in ATTN_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
+    h.update(" ".join(compile_flags()).encode())
     return h.hexdigest()
 
 
@@ -91,6 +98,26 @@ def traffic_for_attention(workload_name):
         return None
 
 
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(x, w, kept_F, budget_s):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import oracle
@@ -99,6 +126,10 @@ def cpu_baseline(x, w, kept_F, budget_s):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = None
     F = kept_F
     t0 = time.perf_counter()
     qd = oracle.decode(x["q"][0:1, 0:1], w.dtype)
@@ -130,6 +161,10 @@ def cpu_baseline(x, w, kept_F, budget_s):
         "value": fl / t_rows / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "blas_threads": int(threads),
+        "os_cpu_count": os.cpu_count(),
+        "cpus_in_affinity": affinity,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"batch 0 head 0 of {w.B}x{w.H}: means+scores+selection for the head "
                    f"({t_sel:.2f} s), attention for the first {len(rows)} of {w.nqb} query "
@@ -260,8 +295,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="final-72k")
-    ap.add_argument("--cold", action="store_true",
-                    help="overwrite a 512 MiB buffer before every timed step (cold L2/MALL)")
+    ap.add_argument("--warm", action="store_true",
+                    help="headline from back-to-back steps (warm L2/MALL); by default every "
+                         "timed step follows a 512 MiB overwrite (cold L2/MALL), and the other "
+                         "mode is reported beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline sample")
@@ -324,7 +361,7 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((B, H, w.Nq), dtype=f32, device=dev)
     stream = torch.cuda.current_stream()
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if args.cold else None
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
     if fused:
         names = ["means_q", "means_k", "scores_select", "attn"]
@@ -348,33 +385,51 @@ def main():
             c()
         if ev: ev[len(calls)].record(stream)
 
+    def measure(cold, steps):
+        """ms per step and mean ms per call.  Cold: each step follows an
+        overwrite of 512 MiB (L2 and MALL hold none of its inputs) and is
+        timed on its own; warm: `steps` steps back to back between two
+        events.  Per-call times come from a second pass with an event before
+        and after every call on the launch stream."""
+        if cold:
+            per = []
+            for _ in range(steps):
+                flush.fill_(0)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                step()
+                b.record(stream)
+                b.synchronize()
+                per.append(a.elapsed_time(b))
+            ms = float(np.mean(per))
+        else:
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(steps):
+                step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+               for _ in range(steps)]
+        for e in evs:
+            if cold:
+                flush.fill_(0)
+            step(e)
+        torch.cuda.synchronize()
+        per_call = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                    for i, n in enumerate(names)}
+        return ms, per_call
+
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # pass 1: whole steps, K of them between two events
-    log(f"[bench] timing {args.steps} steps")
-    if args.cold:
-        per = []
-        for _ in range(args.steps):
-            flush.fill_(0)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            step()
-            b.record(stream)
-            b.synchronize()
-            per.append(a.elapsed_time(b))
-        ms_per_step = float(np.mean(per))
-    else:
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(args.steps):
-            step()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms_per_step = a.elapsed_time(b) / args.steps
+    primary_cold = not args.warm
+    log(f"[bench] timing {args.steps} steps ({'cold' if primary_cold else 'warm'} cache)")
+    ms_per_step, stage_ms = measure(primary_cold, args.steps)
 
     graph_ms = None
     if args.graph:
@@ -396,37 +451,18 @@ def main():
         torch.cuda.synchronize()
         graph_ms = a.elapsed_time(b) / args.steps
 
-    # pass 2: per-kernel durations from events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-           for _ in range(args.steps)]
-    for e in evs:
-        if args.cold:
-            flush.fill_(0)
-        step(e)
-    torch.cuda.synchronize()
-    stage_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-                for i, n in enumerate(names)}
-
-    # the same steps with L2 and MALL overwritten first (512 MiB) before each
-    cold = None
-    if not args.cold:
-        log("[bench] cold-cache pass")
-        fl = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        ce = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-              for _ in range(min(args.steps, 5))]
-        for e in ce:
-            fl.fill_(0)
-            step(e)
-        torch.cuda.synchronize()
-        c_ms = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ce]))
-                for i, n in enumerate(names)}
-        c_sel = sum(c_ms[n] for n in names[:-1])
-        cold = {"ms_per_step": round(sum(c_ms.values()), 4),
-                "selection_us": round(c_sel * 1e3, 2), "attn_us": round(c_ms["attn"] * 1e3, 2),
-                "selection_frac_hbm": round(stage_bytes(w, kept, nqb, nkb) / (c_sel * 1e-3) / 1e9
-                                            / PEAK_HBM_GBPS, 4),
-                "steps": len(ce)}
-        del fl
+    # the other cache mode, labelled, beside the headline
+    other_steps = min(args.steps, 10)
+    log(f"[bench] {'warm' if primary_cold else 'cold'}-cache pass ({other_steps} steps)")
+    o_ms, o_stage = measure(not primary_cold, other_steps)
+    o_sel = sum(o_stage[n] for n in names[:-1])
+    other = {"cache": "warm" if primary_cold else "cold",
+             "ms_per_step": round(o_ms, 4),
+             "selection_us": round(o_sel * 1e3, 2), "attn_us": round(o_stage["attn"] * 1e3, 2),
+             "selection_frac_hbm": round(stage_bytes(w, kept, nqb, nkb) / (o_sel * 1e-3) / 1e9
+                                         / PEAK_HBM_GBPS, 4),
+             "steps": other_steps}
+    del flush
 
     kv_count = cnt.cpu().numpy()
     kv_index = idx.cpu().numpy()
@@ -466,14 +502,14 @@ def main():
         "data": "synthetic (seeded N(0,1) + per-block offsets; see workloads/)",
         "config": {**w.describe(), "block": blk, "kept_blocks": kept, "n_forced_blocks": F,
                    "selected_tflop": flops / 1e12, "dense_tflop": dense_flops / 1e12,
-                   "cache": "cold" if args.cold else "warm",
+                   "cache": "cold" if primary_cold else "warm",
                    "score_select": "fused" if fused else "two-step"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "diagnostics": diag,
-        "cold_cache": cold,
+        "other_cache": other,
         "stages": {
             **{f"{n}_us": round(stage_ms[n] * 1e3, 2) for n in names},
             "attn_tflops": round(attn_tflops, 2),
