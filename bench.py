@@ -2,9 +2,11 @@
 """Benchmark of one SparSTAR attention scale on one MI355X.
 
 A step is the whole hot path over one batch of synthetic input already
-resident in HBM: block means of Q and K, block scores, clip-aware top-k
-selection and block-sparse attention forward, on one stream (with --fused,
-scores and selection run as one launch and the scores stay on chip).  The default workload is the 72,000-token final scale (16 heads,
+resident in HBM: block means of Q and K, block scores with clip-aware top-k
+selection (the screened route: float16 screened scores in a workspace and
+exact scores for the blocks that decide a row; --two-step materialises the
+float32 score matrix instead, with the same selection) and block-sparse
+attention forward, on one stream.  The default workload is the 72,000-token final scale (16 heads,
 D = 128, bf16, keys = 512 text + 72,000 reference + 72,000 current, density
 0.09375).
 
@@ -304,8 +306,9 @@ def main():
                     help="seconds of oracle work for the CPU baseline sample")
     ap.add_argument("--block", type=int, default=128, choices=[32, 64, 128],
                     help="block size in tokens (the pages use 128)")
-    ap.add_argument("--fused", action="store_true",
-                    help="scores and selection in one launch (scores stay on chip) instead of two")
+    ap.add_argument("--two-step", action="store_true",
+                    help="scores (float32 S in HBM) then selection, instead of the screened "
+                         "route (sparstar_select_blocks_from_means, the same selection)")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step recorded as one HIP graph and replayed")
     ap.add_argument("--no-diagnostics", action="store_true",
@@ -354,8 +357,9 @@ def main():
     f32, i32 = torch.float32, torch.int32
     qbar = torch.empty((B, H, nqb, D), dtype=f32, device=dev)
     kbar = torch.empty((B, H, nkb, D), dtype=f32, device=dev)
-    fused = args.fused and nkb <= sp.FUSED_MAX_NKB
+    fused = not args.two_step and nkb <= sp.FUSED_MAX_NKB
     S = None if fused else torch.empty((B, H, nqb, nkb), dtype=f32, device=dev)
+    ws = sp.select_workspace(B, H, nqb, nkb, dev) if fused else None
     cnt = torch.empty((B, H, nqb), dtype=i32, device=dev)
     idx = torch.empty((B, H, nqb, max(1, kept)), dtype=i32, device=dev)
     o = torch.empty_like(q)
@@ -364,11 +368,12 @@ def main():
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
     if fused:
-        names = ["means_q", "means_k", "scores_select", "attn"]
+        names = ["means_q", "means_k", "screened_select", "attn"]
         calls = [lambda: sp.block_means(q, blk, out=qbar),
                  lambda: sp.block_means(k, blk, out=kbar),
                  lambda: sp.select_blocks_from_means(qbar, kbar, F, w.density, max_kept=kept,
-                                                     kv_count=cnt, kv_index=idx),
+                                                     kv_count=cnt, kv_index=idx,
+                                                     workspace=ws),
                  lambda: sp.block_sparse_attn_fwd(q, k, v, cnt, idx, block=blk, out=o, lse=lse)]
     else:
         names = ["means_q", "means_k", "scores", "select", "attn"]
@@ -503,7 +508,7 @@ def main():
         "config": {**w.describe(), "block": blk, "kept_blocks": kept, "n_forced_blocks": F,
                    "selected_tflop": flops / 1e12, "dense_tflop": dense_flops / 1e12,
                    "cache": "cold" if primary_cold else "warm",
-                   "score_select": "fused" if fused else "two-step"},
+                   "score_select": "screened" if fused else "two-step"},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(PKG, "libsparstar.so")
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_HIP = 0, 1, 2, 3
 FP32, BF16 = 0, 1
 BLOCK = 128
-FUSED_MAX_NKB = 2048   # sparstar_select_blocks_from_means keeps a row of scores per q block in LDS
+FUSED_MAX_NKB = 2048   # sparstar_select_blocks_from_means holds a row of screened scores in registers
 
 _i64, _f32, _f64, _vp = ctypes.c_int64, ctypes.c_float, ctypes.c_double, ctypes.c_void_p
 _SIGNATURES = {
@@ -22,7 +22,8 @@ _SIGNATURES = {
     "sparstar_block_scores": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _vp, _vp]),
     "sparstar_select_blocks": (ctypes.c_int, [_vp, _i64, _i64, _i64, _i64, _i64, _f64, _vp, _vp, _i64, _vp]),
     "sparstar_select_blocks_from_means": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _i64,
-                                                         _f64, _vp, _vp, _i64, _vp]),
+                                                         _f64, _vp, _vp, _i64, _vp, _i64, _vp]),
+    "sparstar_select_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64]),
     "sparstar_block_sparse_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64,
                                                       _i64, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
     "sparstar_retained_mass": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp]),
@@ -188,9 +189,24 @@ def select_blocks(S, n_forced_blocks, density, max_kept=None, kv_count=None, kv_
     return kv_count, kv_index
 
 
+def select_workspace_bytes(B, H, nqb, nkb) -> int:
+    return lib().sparstar_select_workspace_bytes(B, H, nqb, nkb)
+
+
+def select_workspace(B, H, nqb, nkb, device):
+    """A workspace for select_blocks_from_means (uint8, 256-byte aligned)."""
+    torch = _torch()
+    n = select_workspace_bytes(B, H, nqb, nkb)
+    if n < 0:
+        raise SparstarError(ERR_UNSUPPORTED, f"no screened route for nkb={nkb}")
+    return torch.empty(max(1, n), dtype=torch.uint8, device=device)
+
+
 def select_blocks_from_means(qbar, kbar, n_forced_blocks, density, tau=None, max_kept=None,
-                             kv_count=None, kv_index=None, stream=None):
-    """Scores and selection in one launch (S stays on chip); nkb <= FUSED_MAX_NKB."""
+                             kv_count=None, kv_index=None, workspace=None, stream=None):
+    """Scores and selection without S in float32 (screened scores in a
+    workspace, exact scores for the few blocks that decide a row);
+    nkb <= FUSED_MAX_NKB.  The selection equals select_blocks(block_scores(...))."""
     torch = _torch()
     B, H, nqb, D = qbar.shape
     nkb = kbar.shape[2]
@@ -200,9 +216,14 @@ def select_blocks_from_means(qbar, kbar, n_forced_blocks, density, tau=None, max
         tau = 1.0 / math.sqrt(D)
     max_kept, kv_count, kv_index = _selection_buffers((B, H, nqb), n_forced_blocks, density, nkb,
                                                       max_kept, kv_count, kv_index, qbar.device)
+    if workspace is None:
+        workspace = select_workspace(B, H, nqb, nkb, qbar.device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
     _check(lib().sparstar_select_blocks_from_means(
         _dev(qbar, "qbar"), _dev(kbar, "kbar"), B, H, nqb, nkb, D, tau, n_forced_blocks, density,
-        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept, _stream(stream)))
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept,
+        _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
     return kv_count, kv_index
 
 

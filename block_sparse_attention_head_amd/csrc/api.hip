@@ -76,7 +76,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 extern "C" {
 
-int32_t sparstar_version(void) { return 10200; }
+int32_t sparstar_version(void) { return 10300; }
 
 const char* sparstar_last_error(void) { return g_err; }
 
@@ -148,16 +148,25 @@ sparstar_status sparstar_select_blocks(const float* S, int64_t B, int64_t H, int
                               kv_count, kv_index, max_kept, static_cast<hipStream_t>(stream));
 }
 
+int64_t sparstar_select_workspace_bytes(int64_t B, int64_t H, int64_t nqb, int64_t nkb) {
+  if (B < 1 || H < 1 || nqb < 1 || nkb < 1 || nkb > fused_select_max_nkb()) return -1;
+  if (B > kMaxI32 / H || nqb > kMaxI32 / (B * H)) return -1;
+  return select_workspace_bytes(B * H, nqb, nkb);
+}
+
 sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float* kbar,
                                                   int64_t B, int64_t H, int64_t nqb, int64_t nkb,
                                                   int64_t D, float tau, int64_t n_forced_blocks,
                                                   double density, int32_t* kv_count,
                                                   int32_t* kv_index, int64_t max_kept,
+                                                  void* workspace, int64_t workspace_bytes,
                                                   void* stream) {
   const char* fn = "sparstar_select_blocks_from_means";
   clear_error();
-  if (!qbar || !kbar || !kv_count || !kv_index) return invalid(fn, "null pointer");
+  if (!qbar || !kbar || !kv_count || !kv_index || !workspace) return invalid(fn, "null pointer");
   if (!aligned16(qbar) || !aligned16(kbar)) return invalid(fn, "qbar and kbar must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return invalid(fn, "workspace must be 256-byte aligned");
   if (nqb < 1 || nkb < 1) return invalid(fn, "nqb and nkb must be >= 1");
   sparstar_status st = check_bhnd(fn, B, H, nqb > nkb ? nqb : nkb, D);
   if (st != SPARSTAR_OK) return st;
@@ -178,8 +187,14 @@ sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float
               "sparstar_select_blocks)", fn, (long long)fused_select_max_nkb());
     return SPARSTAR_ERR_UNSUPPORTED;
   }
+  const int64_t need = select_workspace_bytes(B * H, nqb, nkb);
+  if (workspace_bytes < need) {
+    set_error("%s: workspace_bytes (%lld) < %lld (sparstar_select_workspace_bytes)", fn,
+              (long long)workspace_bytes, (long long)need);
+    return SPARSTAR_ERR_INVALID_ARGUMENT;
+  }
   return launch_scores_select(qbar, kbar, B * H, nqb, nkb, D, tau, n_forced_blocks,
-                              kept - n_forced_blocks, kv_count, kv_index, max_kept,
+                              kept - n_forced_blocks, kv_count, kv_index, max_kept, workspace,
                               static_cast<hipStream_t>(stream));
 }
 

@@ -29,9 +29,12 @@ sparstar_status launch_select_blocks(const float* S, int64_t rows, int64_t nkb, 
 sparstar_status launch_scores_select(const float* qbar, const float* kbar, int64_t BH,
                                      int64_t nqb, int64_t nkb, int64_t D, float tau,
                                      int64_t n_forced, int64_t k, int32_t* kv_count,
-                                     int32_t* kv_index, int64_t max_kept, hipStream_t s);
-// Largest nkb the fused score + selection kernel takes (its score rows live in LDS).
+                                     int32_t* kv_index, int64_t max_kept, void* workspace,
+                                     hipStream_t s);
+// Largest nkb the screened score + selection route takes (a row lives in registers).
 int64_t fused_select_max_nkb();
+// Workspace bytes of the screened route for BH heads of nqb x nkb blocks.
+int64_t select_workspace_bytes(int64_t BH, int64_t nqb, int64_t nkb);
 sparstar_status launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t block,
                                      const int32_t* kv_count, const int32_t* kv_index,

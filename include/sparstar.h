@@ -112,22 +112,34 @@ sparstar_status sparstar_select_blocks(const float* S, int64_t B, int64_t H, int
                                        void* stream);
 
 /*
- * Scores and selection in one pass: the same result as
+ * Scores and selection in one pass (review, "What carries the argument":
+ * Eq. 2 scores, then the clip-aware joint Top-K): the same result as
  * sparstar_block_scores(qbar, kbar, ..., tau, S) followed by
  * sparstar_select_blocks(S, ...), bit for bit, without S in device memory.
- * The score of each (i, j) is formed exactly as sparstar_block_scores forms
- * it, so the two routes rank identically.  Arguments are those of the two
- * calls (qbar [B,H,nqb,D], kbar [B,H,nkb,D] float32; kv_count [B,H,nqb];
- * kv_index [B,H,nqb,max_kept]) with their requirements, and additionally
- * nkb <= 2048 (a row of scores per query block is staged on chip); larger
- * nkb returns SPARSTAR_ERR_UNSUPPORTED.
+ * All scores are first screened at reduced precision with a proven error
+ * bound; only the blocks whose score lies within that bound of a row's k-th
+ * largest are recomputed exactly as sparstar_block_scores forms them, and
+ * the ranking uses those exact values, so both routes select identically.
+ * Arguments are those of the two calls (qbar [B,H,nqb,D], kbar [B,H,nkb,D]
+ * float32; kv_count [B,H,nqb]; kv_index [B,H,nqb,max_kept]) with their
+ * requirements, and additionally nkb <= 2048 (a row of screened scores is
+ * held in registers); larger nkb returns SPARSTAR_ERR_UNSUPPORTED.
+ * workspace: caller-owned device memory of at least
+ * sparstar_select_workspace_bytes(B, H, nqb, nkb) bytes, 256-byte aligned,
+ * used as scratch (the screened scores as float16, nqb x ~nkb per head, and
+ * the key-block norms); its contents before and after the call carry no
+ * meaning.  Two calls in flight at once must not share a workspace.
  */
 sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float* kbar,
                                                   int64_t B, int64_t H, int64_t nqb, int64_t nkb,
                                                   int64_t D, float tau, int64_t n_forced_blocks,
                                                   double density, int32_t* kv_count,
                                                   int32_t* kv_index, int64_t max_kept,
+                                                  void* workspace, int64_t workspace_bytes,
                                                   void* stream);
+/* Workspace bytes sparstar_select_blocks_from_means needs for these sizes;
+ * -1 when the sizes are invalid or nkb > 2048.  Host only. */
+int64_t sparstar_select_workspace_bytes(int64_t B, int64_t H, int64_t nqb, int64_t nkb);
 
 /*
  * Block-sparse forward attention (review, "What carries the argument": only

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_helpers():
-    assert sp.version() == 10200
+    assert sp.version() == 10300
     assert sp.forced_blocks(0) == 0
     assert sp.forced_blocks(1) == 1
     assert sp.forced_blocks(128) == 1
@@ -110,12 +110,14 @@ def test_select_validation():
 
 def test_fused_select_validation():
     f = _lib().sparstar_select_blocks_from_means
-    ok = [FAKE, FAKE, 1, 1, 4, 16, 128, 0.088, 1, 0.25, FAKE, FAKE, 5, NULL]
+    ws = sp.select_workspace_bytes(1, 1, 4, 16)
+    assert ws > 0
+    ok = [FAKE, FAKE, 1, 1, 4, 16, 128, 0.088, 1, 0.25, FAKE, FAKE, 5, FAKE, ws, NULL]
 
     def call(**kw):
         a = list(ok)
         pos = {"qbar": 0, "nqb": 4, "nkb": 5, "D": 6, "tau": 7, "F": 8, "density": 9,
-               "cnt": 10, "max_kept": 12}
+               "cnt": 10, "max_kept": 12, "ws": 13, "ws_bytes": 14}
         for k, v in kw.items():
             a[pos[k]] = v
         return f(*a)
@@ -129,8 +131,15 @@ def test_fused_select_validation():
     _err(call(F=17), sp.ERR_INVALID_ARGUMENT, "n_forced")
     _err(call(density=1.5), sp.ERR_INVALID_ARGUMENT, "density")
     _err(call(max_kept=4), sp.ERR_INVALID_ARGUMENT, "max_kept")
+    _err(call(ws=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(ws=ctypes.c_void_p(4096 + 128)), sp.ERR_INVALID_ARGUMENT, "256-byte")
+    _err(call(ws_bytes=ws - 1), sp.ERR_INVALID_ARGUMENT, "workspace_bytes")
     big = sp.FUSED_MAX_NKB + 1
     _err(call(nkb=big, max_kept=big), sp.ERR_UNSUPPORTED, "nkb")
+    # workspace sizes: float16 screened scores (64 * ceil(nkb / 64) per row) + norms
+    assert sp.select_workspace_bytes(1, 16, 563, 1129) == 16 * 563 * 1152 * 2 + 16 * 1129 * 4
+    assert sp.select_workspace_bytes(1, 1, 4, 2049) == -1
+    assert sp.select_workspace_bytes(0, 1, 4, 16) == -1
     # the largest supported row passes validation up to the launch (not made here)
     assert sp.FUSED_MAX_NKB == 2048
 

@@ -100,6 +100,12 @@ FUSED_CASES = [
     (128, 5, 2048, 4, 0.09375, "normal"), (128, 40, 300, 0, 0.5, "ties"),
     (64, 21, 129, 4, 0.625, "ties"), (128, 9, 200, 10, 0.0, "normal"),
     (128, 9, 65, 65, 0.5, "normal"), (64, 3, 1000, 2, 1.0, "ties"),
+    # groups of near-duplicate key blocks: bands of a few blocks decided on
+    # exact scores, and larger groups that exceed the band capacity
+    (128, 37, 1129, 4, 0.09375, "near"), (64, 40, 600, 3, 0.25, "near"),
+    (128, 20, 2048, 4, 0.1875, "near_wide"), (128, 33, 1129, 4, 0.09375, "scaled"),
+    (128, 18, 300, 4, 0.5, "neg_tau"), (128, 18, 300, 4, 0.5, "zero_tau"),
+    (64, 17, 700, 0, 0.0, "normal"), (128, 21, 1500, 1500, 0.3, "normal"),
 ]
 
 
@@ -107,6 +113,18 @@ def _fused_means(D, nqb, nkb, kind, seed):
     rng = np.random.default_rng(seed)
     qb = (rng.standard_normal((2, 2, nqb, D)) * 0.3).astype(np.float32)
     kb = (rng.standard_normal((2, 2, nkb, D)) * 0.3).astype(np.float32)
+    if kind in ("near", "near_wide"):
+        # every key block is one of few base vectors plus a relative
+        # perturbation of ~1e-6 (near) or ~1e-7 (near_wide): the scores come
+        # in tight clusters of 6 (near) or 40 (near_wide) blocks
+        g = 6 if kind == "near" else 40
+        base = kb[:, :, ::g].repeat(g, axis=2)[:, :, :nkb]
+        eps = 1e-6 if kind == "near" else 1e-7
+        kb = (base * (1 + eps * rng.standard_normal(base.shape))).astype(np.float32)
+    elif kind == "scaled":
+        # means far from unit scale (the bound scales with them)
+        qb = (qb * 3e3).astype(np.float32)
+        kb = (kb * 2e-3).astype(np.float32)
     if kind == "ties":
         # few distinct small dyadic values: many scores are exactly equal
         # (dyadic values: every score is exact, distinct sums stay far apart)
@@ -121,16 +139,17 @@ def test_fused_select_matches_two_step(D, nqb, nkb, F, density, kind):
     log(f"fused select D={D} nqb={nqb} nkb={nkb} F={F} density={density} kind={kind}")
     qb, kb = _fused_means(D, nqb, nkb, kind, seed=nqb * 7 + nkb)
     q_t, k_t = torch.from_numpy(qb).cuda(), torch.from_numpy(kb).cuda()
+    tau = {"neg_tau": -1.0 / math.sqrt(D), "zero_tau": 0.0}.get(kind, 1.0 / math.sqrt(D))
     max_kept = sp.kept_blocks(nkb, F, density) + 2
-    c1, i1 = sp.select_blocks_from_means(q_t, k_t, F, density, max_kept=max_kept)
-    S = sp.block_scores(q_t, k_t)
+    c1, i1 = sp.select_blocks_from_means(q_t, k_t, F, density, tau=tau, max_kept=max_kept)
+    S = sp.block_scores(q_t, k_t, tau=tau)
     c2, i2 = sp.select_blocks(S, F, density, max_kept=max_kept)
     c1, i1, c2, i2 = (t.cpu().numpy() for t in (c1, i1, c2, i2))
     # same scores, same rule: identical to the two-call route
     assert np.array_equal(c1, c2)
     assert np.array_equal(i1, i2)
     # and the oracle's selection up to the near-tie rule
-    ref_S = oracle.block_scores(qb.astype(np.float64), kb.astype(np.float64))
+    ref_S = oracle.block_scores(qb.astype(np.float64), kb.astype(np.float64), tau=tau)
     swaps = check_selection(ref_S, F, density, c1, i1)
     log(f"  {c1.size} rows, {swaps} near-tie swaps")
     if kind == "ties":
