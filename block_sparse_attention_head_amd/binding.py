@@ -24,6 +24,8 @@ _SIGNATURES = {
     "sparstar_select_blocks_from_means": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _i64,
                                                          _f64, _vp, _vp, _i64, _vp, _i64, _vp]),
     "sparstar_select_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64]),
+    "sparstar_select_blocks_from_means_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
+                                                                 _i64, _f64, _vp, _vp, _i64, _vp]),
     "sparstar_block_sparse_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64,
                                                       _i64, _i64, _vp, _vp, _i64, _f32, _vp, _vp, _vp]),
     "sparstar_retained_mass": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp]),
@@ -224,6 +226,27 @@ def select_blocks_from_means(qbar, kbar, n_forced_blocks, density, tau=None, max
         _dev(qbar, "qbar"), _dev(kbar, "kbar"), B, H, nqb, nkb, D, tau, n_forced_blocks, density,
         _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept,
         _dev(workspace, "workspace"), workspace.numel(), _stream(stream)))
+    return kv_count, kv_index
+
+
+def select_blocks_from_means_noalloc(qbar, kbar, n_forced_blocks, density, tau=None,
+                                     max_kept=None, kv_count=None, kv_index=None, stream=None):
+    """select_blocks_from_means without a workspace: the library's own device
+    scratch (64 MiB per GPU) stands in for it, so the call itself allocates
+    nothing (pass kv_count and kv_index to keep it that way).  Calls that
+    overlap in time on one GPU race on that scratch."""
+    torch = _torch()
+    B, H, nqb, D = qbar.shape
+    nkb = kbar.shape[2]
+    _expect(qbar, "qbar", (B, H, nqb, D), torch.float32)
+    _expect(kbar, "kbar", (B, H, nkb, D), torch.float32)
+    if tau is None:
+        tau = 1.0 / math.sqrt(D)
+    max_kept, kv_count, kv_index = _selection_buffers((B, H, nqb), n_forced_blocks, density, nkb,
+                                                      max_kept, kv_count, kv_index, qbar.device)
+    _check(lib().sparstar_select_blocks_from_means_noalloc(
+        _dev(qbar, "qbar"), _dev(kbar, "kbar"), B, H, nqb, nkb, D, tau, n_forced_blocks, density,
+        _dev(kv_count, "kv_count"), _dev(kv_index, "kv_index"), max_kept, _stream(stream)))
     return kv_count, kv_index
 
 

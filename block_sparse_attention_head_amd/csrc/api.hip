@@ -74,6 +74,41 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 }  // namespace
 
+namespace {
+// Arguments of the screened score + selection route (both entry points).
+sparstar_status check_select_from_means(const char* fn, const float* qbar, const float* kbar,
+                                        int64_t B, int64_t H, int64_t nqb, int64_t nkb,
+                                        int64_t D, float tau, int64_t n_forced_blocks,
+                                        double density, const int32_t* kv_count,
+                                        const int32_t* kv_index, int64_t max_kept,
+                                        int64_t* kept_out) {
+  if (!qbar || !kbar || !kv_count || !kv_index) return invalid(fn, "null pointer");
+  if (!aligned16(qbar) || !aligned16(kbar)) return invalid(fn, "qbar and kbar must be 16-byte aligned");
+  if (nqb < 1 || nkb < 1) return invalid(fn, "nqb and nkb must be >= 1");
+  sparstar_status st = check_bhnd(fn, B, H, nqb > nkb ? nqb : nkb, D);
+  if (st != SPARSTAR_OK) return st;
+  if (nqb > kMaxI32 / nkb || B * H > kMaxI32 / nqb) return invalid(fn, "sizes too large");
+  if (!std::isfinite(tau)) return invalid(fn, "tau must be finite");
+  if (n_forced_blocks < 0 || n_forced_blocks > nkb)
+    return invalid(fn, "n_forced_blocks must lie in [0, nkb]");
+  if (!density_ok(density)) return invalid(fn, "density must lie in [0, 1]");
+  const int64_t kept = sparstar_kept_blocks(nkb, n_forced_blocks, density);
+  if (max_kept < kept) {
+    set_error("%s: max_kept (%lld) < kept blocks per row (%lld)", fn, (long long)max_kept,
+              (long long)kept);
+    return SPARSTAR_ERR_INVALID_ARGUMENT;
+  }
+  if (max_kept > kMaxI32) return invalid(fn, "max_kept too large");
+  if (nkb > fused_select_max_nkb()) {
+    set_error("%s: nkb > %lld is not supported (use sparstar_block_scores + "
+              "sparstar_select_blocks)", fn, (long long)fused_select_max_nkb());
+    return SPARSTAR_ERR_UNSUPPORTED;
+  }
+  *kept_out = kept;
+  return SPARSTAR_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int32_t sparstar_version(void) { return 10300; }
@@ -163,30 +198,14 @@ sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float
                                                   void* stream) {
   const char* fn = "sparstar_select_blocks_from_means";
   clear_error();
-  if (!qbar || !kbar || !kv_count || !kv_index || !workspace) return invalid(fn, "null pointer");
-  if (!aligned16(qbar) || !aligned16(kbar)) return invalid(fn, "qbar and kbar must be 16-byte aligned");
+  int64_t kept = 0;
+  sparstar_status st = check_select_from_means(fn, qbar, kbar, B, H, nqb, nkb, D, tau,
+                                               n_forced_blocks, density, kv_count, kv_index,
+                                               max_kept, &kept);
+  if (st != SPARSTAR_OK) return st;
+  if (!workspace) return invalid(fn, "null pointer");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return invalid(fn, "workspace must be 256-byte aligned");
-  if (nqb < 1 || nkb < 1) return invalid(fn, "nqb and nkb must be >= 1");
-  sparstar_status st = check_bhnd(fn, B, H, nqb > nkb ? nqb : nkb, D);
-  if (st != SPARSTAR_OK) return st;
-  if (nqb > kMaxI32 / nkb || B * H > kMaxI32 / nqb) return invalid(fn, "sizes too large");
-  if (!std::isfinite(tau)) return invalid(fn, "tau must be finite");
-  if (n_forced_blocks < 0 || n_forced_blocks > nkb)
-    return invalid(fn, "n_forced_blocks must lie in [0, nkb]");
-  if (!density_ok(density)) return invalid(fn, "density must lie in [0, 1]");
-  const int64_t kept = sparstar_kept_blocks(nkb, n_forced_blocks, density);
-  if (max_kept < kept) {
-    set_error("%s: max_kept (%lld) < kept blocks per row (%lld)", fn, (long long)max_kept,
-              (long long)kept);
-    return SPARSTAR_ERR_INVALID_ARGUMENT;
-  }
-  if (max_kept > kMaxI32) return invalid(fn, "max_kept too large");
-  if (nkb > fused_select_max_nkb()) {
-    set_error("%s: nkb > %lld is not supported (use sparstar_block_scores + "
-              "sparstar_select_blocks)", fn, (long long)fused_select_max_nkb());
-    return SPARSTAR_ERR_UNSUPPORTED;
-  }
   const int64_t need = select_workspace_bytes(B * H, nqb, nkb);
   if (workspace_bytes < need) {
     set_error("%s: workspace_bytes (%lld) < %lld (sparstar_select_workspace_bytes)", fn,
@@ -195,6 +214,33 @@ sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float
   }
   return launch_scores_select(qbar, kbar, B * H, nqb, nkb, D, tau, n_forced_blocks,
                               kept - n_forced_blocks, kv_count, kv_index, max_kept, workspace,
+                              static_cast<hipStream_t>(stream));
+}
+
+sparstar_status sparstar_select_blocks_from_means_noalloc(const float* qbar, const float* kbar,
+                                                          int64_t B, int64_t H, int64_t nqb,
+                                                          int64_t nkb, int64_t D, float tau,
+                                                          int64_t n_forced_blocks, double density,
+                                                          int32_t* kv_count, int32_t* kv_index,
+                                                          int64_t max_kept, void* stream) {
+  const char* fn = "sparstar_select_blocks_from_means_noalloc";
+  clear_error();
+  int64_t kept = 0;
+  sparstar_status st = check_select_from_means(fn, qbar, kbar, B, H, nqb, nkb, D, tau,
+                                               n_forced_blocks, density, kv_count, kv_index,
+                                               max_kept, &kept);
+  if (st != SPARSTAR_OK) return st;
+  const int64_t need = select_workspace_bytes(B * H, nqb, nkb);
+  if (need > select_scratch_bytes()) {
+    set_error("%s: these sizes need %lld bytes of scratch, more than the %lld this entry point "
+              "holds (use sparstar_select_blocks_from_means with a workspace)", fn,
+              (long long)need, (long long)select_scratch_bytes());
+    return SPARSTAR_ERR_UNSUPPORTED;
+  }
+  void* scratch = nullptr;
+  if ((st = select_scratch_pointer(&scratch)) != SPARSTAR_OK) return st;
+  return launch_scores_select(qbar, kbar, B * H, nqb, nkb, D, tau, n_forced_blocks,
+                              kept - n_forced_blocks, kv_count, kv_index, max_kept, scratch,
                               static_cast<hipStream_t>(stream));
 }
 

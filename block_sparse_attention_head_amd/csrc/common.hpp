@@ -35,6 +35,10 @@ sparstar_status launch_scores_select(const float* qbar, const float* kbar, int64
 int64_t fused_select_max_nkb();
 // Workspace bytes of the screened route for BH heads of nqb x nkb blocks.
 int64_t select_workspace_bytes(int64_t BH, int64_t nqb, int64_t nkb);
+// The allocation-free route's device scratch: its size, and its address on
+// the current device (looked up once per device).
+int64_t select_scratch_bytes();
+sparstar_status select_scratch_pointer(void** out);
 sparstar_status launch_attn_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      int64_t BH, int64_t Nq, int64_t Nk, int64_t D, int64_t block,
                                      const int32_t* kv_count, const int32_t* kv_index,

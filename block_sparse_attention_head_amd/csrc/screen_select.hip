@@ -36,6 +36,7 @@
 //     usual row selector.
 // The forward index list is written ascending, -1 padded, with its count.
 #include <cmath>
+#include <mutex>
 
 #include "score_tile.hpp"
 #include "select_row.hpp"
@@ -513,6 +514,53 @@ Layout layout_of(int64_t BH, int64_t nqb, int64_t nkb) {
 }  // namespace
 
 int64_t fused_select_max_nkb() { return kMaxNkb; }
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point: a fixed device array instead of
+// a caller workspace.  Each GPU the library runs on holds its own copy until
+// the process ends; every call on that GPU uses it, so calls that overlap in
+// time on one GPU race.  Nothing in it needs to start at zero (the screening
+// kernel writes every entry the band kernel reads for real blocks).
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int64_t select_scratch_bytes() { return kScratchBytes; }
+
+// The current device's address of `scratch`, looked up once per device (the
+// array's name is only a host-side stand-in; kernels and copies take this).
+sparstar_status select_scratch_pointer(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("sparstar_select_blocks_from_means_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    return SPARSTAR_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("sparstar_select_blocks_from_means_noalloc: device %d beyond the %d supported", dev,
+              kMaxDevices);
+    return SPARSTAR_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      set_error("sparstar_select_blocks_from_means_noalloc: hipGetSymbolAddress: %s",
+                hipGetErrorString(e));
+      return SPARSTAR_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPARSTAR_OK;
+}
 
 int64_t select_workspace_bytes(int64_t BH, int64_t nqb, int64_t nkb) {
   return layout_of(BH, nqb, nkb).total;

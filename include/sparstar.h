@@ -142,6 +142,25 @@ sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float
 int64_t sparstar_select_workspace_bytes(int64_t B, int64_t H, int64_t nqb, int64_t nkb);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments, result and requirements as
+ * sparstar_select_blocks_from_means, without the workspace.  In its place
+ * the library uses a 64 MiB array of its own in device memory, one per GPU it
+ * runs on, held until the process ends; this call allocates nothing.  Sizes
+ * whose sparstar_select_workspace_bytes exceeds 64 MiB return
+ * SPARSTAR_ERR_UNSUPPORTED before anything is enqueued.  Every call on one
+ * GPU uses that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and must not be made.
+ */
+sparstar_status sparstar_select_blocks_from_means_noalloc(const float* qbar, const float* kbar,
+                                                          int64_t B, int64_t H, int64_t nqb,
+                                                          int64_t nkb, int64_t D, float tau,
+                                                          int64_t n_forced_blocks, double density,
+                                                          int32_t* kv_count, int32_t* kv_index,
+                                                          int64_t max_kept, void* stream);
+
+/*
  * Block-sparse forward attention (review, "What carries the argument": only
  * the selected blocks are computed, by a forward-only operator).
  * For every query token t of query block i of (b,h):

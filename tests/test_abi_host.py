@@ -144,6 +144,22 @@ def test_fused_select_validation():
     assert sp.FUSED_MAX_NKB == 2048
 
 
+def test_noalloc_validation():
+    """The allocation-free route refuses sizes beyond its 64 MiB scratch, and
+    bad arguments, before anything is enqueued."""
+    f = _lib().sparstar_select_blocks_from_means_noalloc
+    assert sp.select_workspace_bytes(1, 64, 1000, 2048) > 64 << 20
+    assert sp.select_workspace_bytes(1, 16, 563, 1129) <= 64 << 20
+    _err(f(FAKE, FAKE, 1, 64, 1000, 2048, 128, 0.088, 4, 0.1, FAKE, FAKE, 210, NULL),
+         sp.ERR_UNSUPPORTED, "scratch")
+    _err(f(NULL, FAKE, 1, 1, 4, 16, 128, 0.088, 1, 0.25, FAKE, FAKE, 5, NULL),
+         sp.ERR_INVALID_ARGUMENT, "null")
+    _err(f(FAKE, FAKE, 1, 1, 4, 16, 128, 0.088, 1, 0.25, FAKE, FAKE, 4, NULL),
+         sp.ERR_INVALID_ARGUMENT, "max_kept")
+    _err(f(FAKE, FAKE, 1, 1, 4, 2049, 128, 0.088, 1, 0.25, FAKE, FAKE, 600, NULL),
+         sp.ERR_UNSUPPORTED, "nkb")
+
+
 def test_retained_mass_validation():
     f = _lib().sparstar_retained_mass
     _err(f(FAKE, FAKE, -1, FAKE, NULL), sp.ERR_INVALID_ARGUMENT, "n must be")
