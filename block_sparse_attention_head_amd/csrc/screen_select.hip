@@ -12,11 +12,13 @@
 // anything.  Two kernels:
 //  A. screen_kernel: every score approximated on the bf16 matrix cores from
 //     a two-term split of each mean (x = hi + lo, both bf16; products
-//     hi*hi + hi*lo + lo*hi on v_mfma_f32_16x16x32_bf16, float32
-//     accumulation), scaled by tau and stored as float16 in the workspace;
-//     work items of 48 query blocks x 32 key blocks, so each key-block mean
-//     is read once per 48 query blocks.  The squared norms of the key-block
-//     means go to the workspace too.
+//     hi*hi + hi*lo + lo*hi on v_mfma_f32_32x32x16_bf16, float32
+//     accumulation), scaled by tau and stored as float16 in the workspace.
+//     Forced blocks and the row padding past nkb get the sentinel 0xffff,
+//     and a non-finite value is stored as +NaN (0x7e00), so the selection
+//     sees every ineligible slot as key 0 and every non-finite one above
+//     +inf.  The largest squared norm of the key-block means of each
+//     128-block strip goes to the workspace too.
 //  B. band_select_kernel, one wavefront per query block (row): a rigorous
 //     bound E on |A_ij - F_ij| (A the stored value): the omitted split terms
 //     (<= 3.02 * 2^-16 |q_d k_d|), the float32 accumulation of 3 D products
@@ -40,6 +42,7 @@
 
 #include "score_tile.hpp"
 #include "select_row.hpp"
+#include "tile_common.hpp"
 
 namespace sparstar {
 namespace {
@@ -47,12 +50,12 @@ namespace {
 constexpr int kSWaves = 4;       // wavefronts (rows) per band-selection workgroup
 constexpr int kBandCap = 48;     // band blocks per row decided on exact scores
 constexpr int kMaxNkb = 2048;    // key blocks per row (a row lives in registers)
-constexpr int kBitWords = kMaxNkb / 32;
-constexpr int kScreenRowTiles = 3;   // 16-row tiles per screening work item
-constexpr int kScreenColTiles = 2;   // 16-column tiles per screening work item
+constexpr uint32_t kSentinel16 = 0xffffu;   // float16 bits whose order key is 0
+constexpr uint32_t kNaN16 = 0x7e00u;        // any non-finite screened value
 
-// Order key of float16 bits (NaN excluded beforehand): increasing with the
-// value, -0 just below +0 (membership below is decided on float compares).
+// Order key of float16 bits: increasing with the value, -0 just below +0.
+// Only the sentinel 0xffff maps to 0; +inf maps to 0xfc00 and the stored
+// NaN 0x7e00 to 0xfe00, every finite value to [0x0400, 0xfbff].
 __device__ __forceinline__ uint32_t key16(uint32_t b) {
   return (b & 0x8000u) ? (~b & 0xffffu) : (b | 0x8000u);
 }
@@ -63,18 +66,20 @@ __device__ __forceinline__ float value_of_key16(uint32_t key) {
   return half_bits_to_float((key & 0x8000u) ? (key & 0x7fffu) : (~key & 0xffffu));
 }
 
-// Eight consecutive floats as bf16 hi and lo parts (x = hi + lo + r with
-// |r| <= 2^-16 |x|), and their sum of squares accumulated into ss.
-__device__ __forceinline__ void split8(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo,
-                                       float& ss) {
-  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+// The smallest key of a finite float16 (in [0x0400, 0xfc00], 0xfc00 = +inf)
+// whose value exceeds x (strict) or reaches x (!strict); x finite.  The key
+// of the nearest float16 is at most two steps from it.
+__device__ __forceinline__ uint32_t key_threshold(float x, bool strict) {
+  uint32_t kk = key16(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
+  kk = kk < 0x0400u ? 0x0400u : (kk > 0xfc00u ? 0xfc00u : kk);
+  auto in = [&](uint32_t q) { return strict ? value_of_key16(q) > x : value_of_key16(q) >= x; };
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 h = static_cast<__bf16>(x[e]);
-    hi[e] = h;
-    lo[e] = static_cast<__bf16>(x[e] - static_cast<float>(h));
-    ss = fmaf(x[e], x[e], ss);
-  }
+  for (int it = 0; it < 3; ++it)
+    if (kk < 0xfc00u && !in(kk)) ++kk;
+#pragma unroll
+  for (int it = 0; it < 3; ++it)
+    if (kk > 0x0400u && in(kk - 1)) --kk;
+  return kk;
 }
 
 // DPP lane moves (GFX9 encodings): row_shr:n = 0x110 + n within rows of 16
@@ -108,16 +113,19 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Largest value over the 64 lanes of non-negative floats (compared as bits).
-__device__ __forceinline__ float wave_max_nonneg(float v) {
-  int x = __float_as_int(v);
-  x = max(x, dpp_i<0x111>(x, x));
-  x = max(x, dpp_i<0x112>(x, x));
-  x = max(x, dpp_i<0x114>(x, x));
-  x = max(x, dpp_i<0x118>(x, x));
-  x = max(x, dpp_i<0x142, 0xa>(x, x));
-  x = max(x, dpp_i<0x143, 0xc>(x, x));
-  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
+// Largest and smallest of an unsigned value over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+  int x = static_cast<int>(v);
+  x = static_cast<int>(max(static_cast<uint32_t>(x), static_cast<uint32_t>(dpp_i<0x111>(x, x))));
+  x = static_cast<int>(max(static_cast<uint32_t>(x), static_cast<uint32_t>(dpp_i<0x112>(x, x))));
+  x = static_cast<int>(max(static_cast<uint32_t>(x), static_cast<uint32_t>(dpp_i<0x114>(x, x))));
+  x = static_cast<int>(max(static_cast<uint32_t>(x), static_cast<uint32_t>(dpp_i<0x118>(x, x))));
+  x = static_cast<int>(max(static_cast<uint32_t>(x), static_cast<uint32_t>(dpp_i<0x142, 0xa>(x, x))));
+  x = static_cast<int>(max(static_cast<uint32_t>(x), static_cast<uint32_t>(dpp_i<0x143, 0xc>(x, x))));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
+}
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+  return ~wave_max_u(~v);
 }
 
 // One level of a radix select from the top: hist[b] counts the candidates
@@ -140,18 +148,21 @@ __device__ __forceinline__ int radix_level(const uint32_t* hist, int lane, int k
   return 255 - __builtin_amdgcn_readlane(4 * lane + j, L);
 }
 
-// The k-th largest of the nonzero 16-bit keys of a row (k >= 1 and at most
-// that many nonzero keys), by a two-level radix select over per-wave LDS
-// histograms of 256 bins.
-template <int C>
-__device__ __forceinline__ uint32_t kth_largest16(const uint32_t (&key)[C], int k, int lane,
+// The k-th largest of the nonzero 16-bit keys of a row (k >= 1, at most that
+// many nonzero keys, all of them >= 0x0400), by a two-level radix select over
+// a per-wave LDS histogram of 256 bins plus one spare bin per lane.  Key 0
+// lands in bin 255, which holds no nonzero key, so it is never reached.  In
+// the second level the keys outside the chosen high-byte bin go to their
+// lane's spare bin, so the atomics need no branch and do not collide.
+template <int CL>
+__device__ __forceinline__ uint32_t kth_largest16(const uint32_t (&key)[CL], int k, int lane,
                                                  uint32_t* hist) {
   // level 1: high byte
   *reinterpret_cast<u32x4*>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
+  hist[256 + lane] = 0u;
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int c = 0; c < C; ++c)
-    if (key[c] != 0u) atomicAdd(&hist[255 - (key[c] >> 8)], 1u);
+  for (int s = 0; s < CL; ++s) atomicAdd(&hist[255 - (key[s] >> 8)], 1u);
   __builtin_amdgcn_wave_barrier();
   int above = 0;
   const uint32_t hi8 = static_cast<uint32_t>(radix_level(hist, lane, k, &above));
@@ -160,8 +171,10 @@ __device__ __forceinline__ uint32_t kth_largest16(const uint32_t (&key)[C], int 
   *reinterpret_cast<u32x4*>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
-  for (int c = 0; c < C; ++c)
-    if (key[c] != 0u && (key[c] >> 8) == hi8) atomicAdd(&hist[255 - (key[c] & 0xffu)], 1u);
+  for (int s = 0; s < CL; ++s) {
+    const bool in = (key[s] >> 8) == hi8;
+    atomicAdd(&hist[in ? 255 - (key[s] & 0xffu) : 256 + lane], 1u);
+  }
   __builtin_amdgcn_wave_barrier();
   int above2 = 0;
   const uint32_t lo8 = static_cast<uint32_t>(radix_level(hist, lane, k - above, &above2));
@@ -169,127 +182,202 @@ __device__ __forceinline__ uint32_t kth_largest16(const uint32_t (&key)[C], int 
   return (hi8 << 8) | lo8;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) x = fmaxf(x, __shfl_xor(x, d));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) x += __shfl_xor(x, d);
-  return x;
-}
-
 // ---------------------------------------------------------------------------
 // A. screening
 // ---------------------------------------------------------------------------
-// One wavefront per workgroup, exactly as many as the GPU holds at once; each
-// takes a contiguous run of work items (strip-major, so its q operands are
-// reloaded only when the 48-row strip changes).  Item = 48 query blocks x 32
-// key blocks: per 16-column tile, the key means are split once and multiply
-// all three 16-row tiles; the next tile's key means load while the current
-// one is on the matrix cores.
-template <int D>
-__global__ __launch_bounds__(64) void screen_kernel(
-    const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int strips,
-    int pairs, int64_t items, float tau, int ws_stride, uint16_t* __restrict__ app,
-    float* __restrict__ kn2) {
-  constexpr int KS = D / 32;
-  const int64_t per = (items + gridDim.x - 1) / gridDim.x;
-  const int64_t it0 = blockIdx.x * per;
-  const int64_t it1 = it0 + per < items ? it0 + per : items;
-  const int lane = threadIdx.x, lr = lane % 16, lg = lane / 16;
-  const int ntk = (nkb + 15) / 16;
+// One workgroup of four wavefronts per tile of 128 query blocks x 128 key
+// blocks of one head, on v_mfma_f32_32x32x16_bf16 (S^T = Kbar Qbar^T: the
+// key means are the A operand).  Every global access is a run of whole
+// 16-byte pieces, consecutive lanes on consecutive bytes, and LDS turns the
+// data around:
+//  * each wavefront reads its 32 query means (16 KiB, contiguous) into LDS
+//    as float32 and takes back its MFMA operand slices, split into bf16 hi
+//    and lo parts (x = hi + lo + r, |r| <= 2^-16 |x|);
+//  * the workgroup then reads the tile's 128 key means (contiguous) and
+//    keeps them in LDS split the same way, rows of one block with an XOR
+//    swizzle of the 16-byte chunks;
+//  * each lane ends with 4 adjacent key blocks of one query block per
+//    register group; two 32 x 32 tiles go through a per-wavefront LDS patch
+//    and leave as 128-byte row pieces.
+// The workspace rows are 128 * cstrips wide, so the tiles cover every slot.
+// Tiles are numbered head-major and dealt out so that the workgroups on one
+// XCD (workgroups go round-robin over the 8 XCDs) work on the same heads,
+// whose means then sit in that XCD's L2.
+constexpr int kScrWaves = 4;
+constexpr int kScrRows = 32 * kScrWaves;   // query blocks per tile
+constexpr int kScrCols = 128;              // key blocks per tile (one strip)
 
-  // key-mean operands of column tile jt (lane (lr, lg): block 16 jt + lr, the
-  // same dimensions as the q operands), clamped to a valid block
-  auto load_b = [&](int64_t bh_, int jt, f32x4 (&kr)[2 * KS]) {
-    const float* kp = kbar + (bh_ * nkb + min(16 * jt + lr, nkb - 1)) * static_cast<int64_t>(D) + 8 * lg;
+template <int D>
+__global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, int nqb, int nkb, int nf,
+    int rstrips, int cstrips, int tiles, int per_xcd, float tau, int ws_stride,
+    uint16_t* __restrict__ app, float* __restrict__ kmaxp) {
+  constexpr int NT = 64 * kScrWaves;
+  constexpr int KS = D / 16;                    // k-steps of 16 dimensions
+  constexpr int CPB = D / 4;                    // float4 chunks per mean (query or key block)
+  constexpr int KLOADS = kScrCols * CPB / NT;   // float4 loads per thread, key means
+  constexpr int QLOADS = 32 * CPB / 64;         // float4 loads per lane, query means
+  constexpr int RB = D * 2;                     // bytes per LDS key row (bf16)
+  constexpr int QRB = D * 4;                    // bytes per LDS query row (float32)
+  static_assert(kScrWaves * 32 * QRB <= 2 * kScrCols * RB, "query staging fits the key region");
+  // key region: hi rows then lo rows; before that it stages the query means
+  __shared__ __attribute__((aligned(16))) unsigned char s_key[2 * kScrCols * RB];
+  __shared__ __attribute__((aligned(16))) unsigned char s_out[kScrWaves][32 * 128];
+  // the strip's largest squared norm, in wavefront 0's patch before its first use
+  // (80 KiB in all, so that two workgroups share a CU)
+  uint32_t* const s_kmax = reinterpret_cast<uint32_t*>(s_out[0]);
+  unsigned char* const s_hi = s_key;
+  unsigned char* const s_lo = s_key + kScrCols * RB;
+
+  const int L = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (L >= tiles) return;                       // whole workgroup, before any barrier
+  const int per_head = rstrips * cstrips;
+  const int64_t bh = L / per_head;
+  const int rs = (L - static_cast<int>(bh) * per_head) / cstrips;
+  const int cs = L - static_cast<int>(bh) * per_head - rs * cstrips;
+  const int t = threadIdx.x, lane = t % 64, w = t / 64;
+  const int c0 = cs * kScrCols;
+  const int q0 = rs * kScrRows + 32 * w;        // this wavefront's first query block
+  if (t == 0) *s_kmax = 0u;
+
+  // global reads, all issued up front: query means (load i, lane l -> chunk
+  // 64 i + l of the wavefront's 32 rows) and key means (load i, thread t ->
+  // chunk t + NT i of the tile's 128 rows); rows past the end repeat the last
+  f32x4 qg[QLOADS], kg[KLOADS];
+  {
+    const float* qp = qbar + bh * static_cast<int64_t>(nqb) * D;
+#pragma unroll
+    for (int i = 0; i < QLOADS; ++i) {
+      const int c = 64 * i + lane;
+      const int r = min(q0 + c / CPB, nqb - 1);
+      qg[i] = *reinterpret_cast<const f32x4*>(qp + static_cast<int64_t>(r) * D + 4 * (c % CPB));
+    }
+    const float* kp = kbar + bh * static_cast<int64_t>(nkb) * D;
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int c = t + NT * i;
+      const int b = min(c0 + c / CPB, nkb - 1);
+      kg[i] = *reinterpret_cast<const f32x4*>(kp + static_cast<int64_t>(b) * D + 4 * (c % CPB));
+    }
+  }
+
+  // query means through LDS (float32 rows, chunk ^ (row % 16)) into the
+  // operand layout: lane l holds query block q0 + l % 32, dimensions
+  // 16 ks + 8 (l / 32) + [0, 8)
+  bf16x8 a_hi[KS], a_lo[KS];
+  {
+    unsigned char* qs = s_key + w * 32 * QRB;
+#pragma unroll
+    for (int i = 0; i < QLOADS; ++i) {
+      const int c = 64 * i + lane, r = c / CPB, ch = c % CPB;
+      *reinterpret_cast<f32x4*>(qs + r * QRB + (ch ^ (r & 15)) * 16) = qg[i];
+    }
+    __syncthreads();
+    const int r = lane % 32;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      kr[2 * ks] = *reinterpret_cast<const f32x4*>(kp + 32 * ks);
-      kr[2 * ks + 1] = *reinterpret_cast<const f32x4*>(kp + 32 * ks + 4);
+      const int ch = 4 * ks + 2 * (lane / 32);
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(qs + r * QRB + (ch ^ (r & 15)) * 16);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(qs + r * QRB + ((ch + 1) ^ (r & 15)) * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = e < 4 ? x0[e] : x1[e - 4];
+        const __bf16 hb = static_cast<__bf16>(x);
+        a_hi[ks][e] = hb;
+        a_lo[ks][e] = static_cast<__bf16>(x - static_cast<float>(hb));
+      }
     }
-  };
-  auto item_start = [&](int64_t it, int64_t& bh_, int& jt) {
-    const int64_t hs = it / pairs;
-    bh_ = hs / strips;
-    jt = kScreenColTiles * static_cast<int>(it - hs * pairs);
-  };
-
-  int64_t cur_strip = -1;
-  bf16x8 qa_hi[kScreenRowTiles][KS], qa_lo[kScreenRowTiles][KS];
-  f32x4 kr[2 * KS];
-  if (it0 < it1) {
-    int64_t b0;
-    int j0;
-    item_start(it0, b0, j0);
-    load_b(b0, j0, kr);
+    __syncthreads();                            // the region is the key tile's next
   }
-  for (int64_t it = it0; it < it1; ++it) {
-    const int64_t hs = it / pairs;               // (b*h) * strips + strip
-    const int pair = static_cast<int>(it - hs * pairs);
-    const int64_t bh = hs / strips;
-    const int r0 = static_cast<int>(hs - bh * strips) * 16 * kScreenRowTiles;
-    if (hs != cur_strip) {
-      // A operands: lane (lr, lg) holds row r0 + 16 t + lr, dimensions 32 ks + 8 lg + [0, 8)
+
+  // key means split into LDS (bf16 rows, 16-byte chunk ^ (row % 16) for
+  // D = 128, ^ ((row / 2) % 8) for D = 64); from the first row strip, the
+  // largest squared norm of the strip (rows past nkb repeat the last block)
 #pragma unroll
-      for (int t = 0; t < kScreenRowTiles; ++t) {
-        const float* qp = qbar + (bh * nqb + min(r0 + 16 * t + lr, nqb - 1)) * static_cast<int64_t>(D) + 8 * lg;
-        float ss = 0.f;
+  for (int i = 0; i < KLOADS; ++i) {
+    const int c = t + NT * i, bl = c / CPB, ch = c % CPB;
+    bf16x4 h, l;
+    float ss = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          split8(*reinterpret_cast<const f32x4*>(qp + 32 * ks),
-                 *reinterpret_cast<const f32x4*>(qp + 32 * ks + 4), qa_hi[t][ks], qa_lo[t][ks], ss);
-      }
-      cur_strip = hs;
+    for (int e = 0; e < 4; ++e) {
+      const float x = kg[i][e];
+      const __bf16 hb = static_cast<__bf16>(x);
+      h[e] = hb;
+      l[e] = static_cast<__bf16>(x - static_cast<float>(hb));
+      ss = fmaf(x, x, ss);
     }
-#pragma unroll 1
-    for (int c = 0; c < kScreenColTiles; ++c) {
-      const int jt = kScreenColTiles * pair + c;
-      if (jt >= ntk) break;
-      const int jc = 16 * jt + lr;
-      // the next tile of this item, else the first tile of the next item
-      f32x4 kn[2 * KS];
-      {
-        int64_t nbh = bh;
-        int njt = jt + 1;
-        if (c + 1 == kScreenColTiles || njt >= ntk) item_start(it + 1 < it1 ? it + 1 : it, nbh, njt);
-        load_b(nbh, njt, kn);
-      }
-      f32x4 acc[kScreenRowTiles];
+    const int sw = D == 128 ? (bl & 15) : ((bl >> 1) & 7);
+    const int off = bl * RB + ((ch / 2) ^ sw) * 16 + (ch & 1) * 8;
+    *reinterpret_cast<bf16x4*>(s_hi + off) = h;
+    *reinterpret_cast<bf16x4*>(s_lo + off) = l;
+    if (rs == 0) {
 #pragma unroll
-      for (int t = 0; t < kScreenRowTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      float kss = 0.f;
+      for (int d = 1; d < CPB; d <<= 1) ss += __shfl_xor(ss, d);
+      if (ch == 0) atomicMax(s_kmax, __float_as_uint(ss));    // ss >= 0: bits order as values
+    }
+  }
+  __syncthreads();
+  if (rs == 0 && t == 0) kmaxp[bh * cstrips + cs] = __uint_as_float(*s_kmax);
+
+  // pairs of 32 x 32 tiles of S^T: tile u, lane l, register 4 j + e = key
+  // block 32 u + 8 j + 4 (l / 32) + e of the pair, query block q0 + l % 32
+  unsigned char* const os = s_out[w];
+#pragma unroll 1
+  for (int p = 0; p < kScrCols / 64; ++p) {
+    f32x16 acc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int bl = 64 * p + 32 * u + lane % 32;
+      const int sw = D == 128 ? (bl & 15) : ((bl >> 1) & 7);
+      bf16x8 kh[KS], kl[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        bf16x8 bh8, bl8;
-        split8(kr[2 * ks], kr[2 * ks + 1], bh8, bl8, kss);
-#pragma unroll
-        for (int t = 0; t < kScreenRowTiles; ++t) {
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_hi[t][ks], bh8, acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_hi[t][ks], bl8, acc[t], 0, 0, 0);
-          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa_lo[t][ks], bh8, acc[t], 0, 0, 0);
-        }
+        const int off = bl * RB + ((2 * ks + lane / 32) ^ sw) * 16;
+        kh[ks] = *reinterpret_cast<const bf16x8*>(s_hi + off);
+        kl[ks] = *reinterpret_cast<const bf16x8*>(s_lo + off);
       }
-      if (jc < nkb) {
-        // acc[t][r] = A(row r0 + 16 t + 4 lg + r, block jc)
+      acc[u] = f32x16{};
 #pragma unroll
-        for (int t = 0; t < kScreenRowTiles; ++t)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = r0 + 16 * t + 4 * lg + r;
-            if (i < nqb)
-              app[(bh * nqb + i) * static_cast<int64_t>(ws_stride) + jc] =
-                  __builtin_bit_cast(uint16_t, static_cast<_Float16>(tau * acc[t][r]));
-          }
+      for (int ks = 0; ks < KS; ++ks) {
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[ks], a_hi[ks], acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[ks], a_hi[ks], acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[ks], a_lo[ks], acc[u], 0, 0, 0);
       }
-      kss += __shfl_xor(kss, 16);
-      kss += __shfl_xor(kss, 32);
-      if (r0 == 0 && jc < nkb && lg == 0) kn2[bh * nkb + jc] = kss;
-#pragma unroll
-      for (int x = 0; x < 2 * KS; ++x) kr[x] = kn[x];
     }
+    // patch: 32 query rows x 64 keys of float16 (128 bytes), chunk ^ (row % 8);
+    // forced blocks and blocks past nkb become the sentinel
+    {
+      const int r = lane % 32;
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kb0 = c0 + 64 * p + 32 * u + 8 * j + 4 * (lane / 32);
+          uint32_t h[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t b = __builtin_bit_cast(uint16_t, static_cast<_Float16>(tau * acc[u][4 * j + e]));
+            if ((b & 0x7c00u) == 0x7c00u) b = kNaN16;           // inf or NaN
+            const int jb = kb0 + e;
+            h[e] = (jb < nf || jb >= nkb) ? kSentinel16 : b;
+          }
+          const int ch = 4 * u + j;
+          *reinterpret_cast<u32x2*>(os + r * 128 + (ch ^ (r & 7)) * 16 + 8 * (lane / 32)) =
+              u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);         // lgkmcnt(0): the patch is written
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = 64 * i + lane, r = c / 8, ch = c % 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(os + r * 128 + (ch ^ (r & 7)) * 16);
+      const int iq = q0 + r;
+      if (iq < nqb)
+        *reinterpret_cast<u32x4*>(app + (bh * nqb + iq) * static_cast<int64_t>(ws_stride) + c0 +
+                                  64 * p + 8 * ch) = v;
+    }
+    __builtin_amdgcn_wave_barrier();            // the patch is read before the next pair
   }
 }
 
@@ -297,22 +385,25 @@ __global__ __launch_bounds__(64) void screen_kernel(
 // B. band selection
 // ---------------------------------------------------------------------------
 // One wavefront per query block (row), kSWaves independent rows per
-// workgroup.  The row's screened values live in registers (slot c of lane l
-// = block l + 64 c).  The exact scores of its band come from fp64 tiles laid
-// out as the score kernel lays them out: the A operand holds the 16 rows of
-// the row's 16-row tile (this row at its own position), the B operand holds
-// band blocks; only this row's results are kept.
-template <int D, int C>
-__global__ __launch_bounds__(64 * kSWaves, C > 18 ? 2 : 4) void band_select_kernel(
+// workgroup.  Lane l owns the CL consecutive blocks CL l .. CL l + CL - 1 of
+// the row (keys in registers, sets of them as CL-bit masks), so counts and
+// the ascending output need one prefix sum over lanes, not one per slot.
+// The exact scores of the band come from fp64 tiles laid out as the score
+// kernel lays them out: the A operand holds the 16 rows of the row's 16-row
+// tile (this row at its own position), the B operand holds band blocks; only
+// this row's results are kept.
+template <int D, int CL>
+__global__ __launch_bounds__(64 * kSWaves, CL > 18 ? 2 : 4) void band_select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t rows, int nqb, int nkb,
-    float tau, int nf, int k, const uint16_t* __restrict__ app, const float* __restrict__ kn2,
-    int ws_stride, int stride, int32_t* __restrict__ cnt, int32_t* __restrict__ idx,
+    float tau, int nf, int k, const uint16_t* __restrict__ app, const float* __restrict__ kmaxp,
+    int cstrips, int ws_stride, int stride, int32_t* __restrict__ cnt, int32_t* __restrict__ idx,
     int max_kept) {
+  static_assert(CL % 2 == 0 && CL <= 32, "keys per lane: even, one 32-bit mask");
   extern __shared__ float s_exact_rows[];          // [kSWaves][stride]: exact route only
-  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSWaves][256];
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSWaves][256 + 64];
   __shared__ float s_bandF[kSWaves][kBandCap];
   __shared__ int32_t s_bandC[kSWaves][kBandCap];
-  __shared__ uint32_t s_chosen[kSWaves][kBitWords];
+  __shared__ uint32_t s_chosen[kSWaves][64];
 
   const int w = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kSWaves + w;
@@ -322,125 +413,113 @@ __global__ __launch_bounds__(64 * kSWaves, C > 18 ? 2 : 4) void band_select_kern
   const int lr = lane % 16, lg = lane / 16;
   const float* qh = qbar + bh * static_cast<int64_t>(nqb) * D;
   const float* kh = kbar + bh * static_cast<int64_t>(nkb) * D;
-  const uint64_t lt = lanemask_lt(lane);
   int32_t* out = idx + row * static_cast<int64_t>(max_kept);
   const double tau_d = static_cast<double>(tau);
+  const int j0 = CL * lane;                         // this lane's first block
 
-  // all loads first: the row's screened values, the key-block norms of the
-  // head, and this query mean
-  uint32_t raw[C];
-  float kv2[C];
-  float qx[D / 64];
+  // all loads first: the lane's screened values (CL / 2 words), the strip
+  // maxima of the squared key norms, this query mean
+  uint32_t wv[CL / 2];
   {
-    const uint16_t* arow = app + row * static_cast<int64_t>(ws_stride);
+    const uint32_t* arow = reinterpret_cast<const uint32_t*>(app + row * static_cast<int64_t>(ws_stride)) +
+                           (CL / 2) * lane;
 #pragma unroll
-    for (int c = 0; c < C; ++c) raw[c] = arow[lane + 64 * c];   // inside the workspace row
-#pragma unroll
-    for (int c = 0; c < C; ++c) kv2[c] = kn2[bh * nkb + min(lane + 64 * c, nkb - 1)];
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) qx[e] = qh[static_cast<int64_t>(i) * D + lane + 64 * e];
+    for (int s = 0; s < CL / 2; ++s) wv[s] = arow[s];
   }
-  // raw[c] becomes the slot's order key (0 for forced and past-the-end
-  // slots); its value is recovered from the key when needed
-  bool bad = false;
-  float amax = 0.f, kmax2 = 0.f;
+  const float kmx2 = lane < cstrips ? kmaxp[bh * cstrips + lane] : 0.f;
+  float qx[D / 64];
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int j = lane + 64 * c;
-    const bool el = static_cast<unsigned>(j - nf) < static_cast<unsigned>(nkb - nf);
-    const float av = half_bits_to_float(raw[c]);
-    kmax2 = fmaxf(kmax2, kv2[c]);
-    if (el) {
-      bad = bad || !(fabsf(av) <= 65504.f);
-      amax = fmaxf(amax, fabsf(av));
-    }
-    raw[c] = el ? key16(raw[c]) : 0u;
+  for (int e = 0; e < D / 64; ++e) qx[e] = qh[static_cast<int64_t>(i) * D + lane + 64 * e];
+
+  // order keys (0 = ineligible); the largest key and the smallest nonzero one
+  uint32_t key[CL];
+  uint32_t kbig = 0u, ksmall_m1 = 0xffffu;
+#pragma unroll
+  for (int s = 0; s < CL; ++s) {
+    key[s] = key16((s & 1) ? (wv[s / 2] >> 16) : (wv[s / 2] & 0xffffu));
+    kbig = max(kbig, key[s]);
+    ksmall_m1 = min(ksmall_m1, (key[s] - 1u) & 0xffffu);   // key 0 -> 0xffff
   }
-  const uint32_t (&key)[C] = raw;
-  auto val = [&](int c) { return value_of_key16(key[c]); };
   float qss = 0.f;
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) qss = fmaf(qx[e], qx[e], qss);
 
-  bool full_exact = __ballot(bad) != 0;             // non-finite screened value
-  float lo = INFINITY, hi = INFINITY;
+  kbig = wave_max_u(kbig);
+  bool full_exact = kbig >= 0xfc00u;                 // a non-finite screened value
+  uint32_t above_m = 0u, band_m = 0u;                // CL-bit masks of this lane's blocks
   bool exact = false;
   if (!full_exact && k > 0) {
-    amax = wave_max_nonneg(amax);
-    const float kmax = sqrtf(wave_max_nonneg(kmax2)) * 1.0001f;
+    const uint32_t ksmall = wave_min_u(ksmall_m1) + 1u;   // >= 0x0400: k > 0 eligible keys exist
+    const float amax = fmaxf(value_of_key16(kbig), -value_of_key16(ksmall));
+    const float kmax = sqrtf(__uint_as_float(wave_max_u(__float_as_uint(kmx2)))) * 1.0001f;
     const float qn = sqrtf(wave_sum_f(qss)) * 1.0001f;
-    const float t = value_of_key16(kth_largest16<C>(key, k, lane, s_hist[w]));
+    const float t = value_of_key16(kth_largest16<CL>(key, k, lane, s_hist[w]));
     const float E = 1.2e-4f * fabsf(tau) * qn * kmax + 6e-4f * amax + 1e-7f;
-    lo = t - 2.f * E;
-    hi = t + 2.f * E;
-    int n_in = 0, m = 0;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const bool el = key[c] != 0u;
-      const float av = val(c);
-      n_in += wave_count(el && av > hi);
-      m += wave_count(el && av >= lo && av <= hi);
-    }
-    const int need = k - n_in;                      // 1 <= need <= m (the k-th lies in the band)
-    exact = m > need;
-    if (exact && (m > kBandCap || !(E < INFINITY))) {
+    const float lo = t - 2.f * E, hi = t + 2.f * E;
+    if (!(E < INFINITY) || !(fabsf(lo) < INFINITY) || !(fabsf(hi) < INFINITY)) {
       full_exact = true;
-    } else if (exact) {
-      // the band's blocks, ascending, into LDS
-      int pos = 0;
+    } else {
+      // keys of values > hi, and of values >= lo (klo >= 0x0400 > key 0)
+      const uint32_t khi = key_threshold(hi, true), klo = key_threshold(lo, false);
+      uint32_t ge_m = 0u;
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const float av = val(c);
-        const bool in = key[c] != 0u && av >= lo && av <= hi;
-        const uint64_t mk = __ballot(in);
-        if (in) s_bandC[w][pos + __popcll(mk & lt)] = lane + 64 * c;
-        pos += __popcll(mk);
+      for (int s = 0; s < CL; ++s) {
+        above_m |= (key[s] >= khi ? 1u : 0u) << s;
+        ge_m |= (key[s] >= klo ? 1u : 0u) << s;
       }
-      __builtin_amdgcn_wave_barrier();
-      // exact scores of the band, 16 blocks per fp64 tile
-      const int i0 = i & ~15, rpos = i - i0;
-      f32x4 qv[D / 16];
-      load_operands<D>(qh + static_cast<int64_t>(min(i0 + lr, nqb - 1)) * D + 4 * lg, qv);
-      for (int c0 = 0; c0 < m; c0 += 16) {
-        const int col = s_bandC[w][min(c0 + lr, m - 1)];
-        f32x4 kq[D / 16];
-        load_operands<D>(kh + static_cast<int64_t>(col) * D + 4 * lg, kq);
-        const f64x4 acc = score_tile16<D>(qv, kq);
-        // fp64 tile layout: lane (lr, lg) holds rows lg + 4 r of column lr
-        if (lg == (rpos & 3) && c0 + lr < m) s_bandF[w][c0 + lr] = static_cast<float>(tau_d * acc[rpos >> 2]);
+      band_m = ge_m & ~above_m;
+      const int packed = wave_inclusive_scan(__popc(above_m) | (__popc(band_m) << 16));
+      const int tot = __builtin_amdgcn_readlane(packed, 63);
+      const int n_in = tot & 0xffff, m = tot >> 16;
+      const int need = k - n_in;                     // 1 <= need <= m (the k-th lies in the band)
+      exact = m > need;
+      if (exact && m > kBandCap) {
+        full_exact = true;
+      } else if (exact) {
+        // the band's blocks into LDS, each lane's in order after those of the lanes below
+        int pos = ((packed >> 16) & 0xffff) - __popc(band_m);
+        for (uint32_t x = band_m; x; x &= x - 1u) s_bandC[w][pos++] = j0 + __builtin_ctz(x);
+        s_chosen[w][lane] = 0u;
+        __builtin_amdgcn_wave_barrier();
+        // exact scores of the band, 16 blocks per fp64 tile
+        const int i0 = i & ~15, rpos = i - i0;
+        f32x4 qv[D / 16];
+        load_operands<D>(qh + static_cast<int64_t>(min(i0 + lr, nqb - 1)) * D + 4 * lg, qv);
+        for (int c0 = 0; c0 < m; c0 += 16) {
+          const int col = s_bandC[w][min(c0 + lr, m - 1)];
+          f32x4 kq[D / 16];
+          load_operands<D>(kh + static_cast<int64_t>(col) * D + 4 * lg, kq);
+          const f64x4 acc = score_tile16<D>(qv, kq);
+          // fp64 tile layout: lane (lr, lg) holds rows lg + 4 r of column lr
+          if (lg == (rpos & 3) && c0 + lr < m) s_bandF[w][c0 + lr] = static_cast<float>(tau_d * acc[rpos >> 2]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        // keep the best `need` of the band: higher F first, then the lower index
+        const float fe = lane < m ? s_bandF[w][lane] : 0.f;
+        const int ce = lane < m ? s_bandC[w][lane] : 0;
+        int rank = 0;
+        for (int e = 0; e < m; ++e) {
+          const float f2 = s_bandF[w][e];
+          const int c2 = s_bandC[w][e];
+          rank += (f2 > fe || (f2 == fe && c2 < ce)) ? 1 : 0;
+        }
+        if (lane < m && rank < need) atomicOr(&s_chosen[w][ce / CL], 1u << (ce % CL));
+        __builtin_amdgcn_wave_barrier();
+        band_m = s_chosen[w][lane];
       }
-      __builtin_amdgcn_wave_barrier();
-      // keep the best `need` of the band: higher F first, then the lower index
-      for (int x = lane; x < kBitWords; x += 64) s_chosen[w][x] = 0u;
-      __builtin_amdgcn_wave_barrier();
-      const float fe = lane < m ? s_bandF[w][lane] : 0.f;
-      const int ce = lane < m ? s_bandC[w][lane] : 0;
-      int rank = 0;
-      for (int e = 0; e < m; ++e) {
-        const float f2 = s_bandF[w][e];
-        const int c2 = s_bandC[w][e];
-        rank += (f2 > fe || (f2 == fe && c2 < ce)) ? 1 : 0;
-      }
-      if (lane < m && rank < need) atomicOr(&s_chosen[w][ce >> 5], 1u << (ce & 31));
-      __builtin_amdgcn_wave_barrier();
     }
   }
 
   if (!full_exact) {
     for (int p = lane; p < nf; p += 64) out[p] = p;
-    int base = nf;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      if (64 * c >= nkb) break;
-      const int j = lane + 64 * c;
-      const float av = val(c);
-      const bool take = key[c] != 0u &&
-                        (av > hi || (av >= lo && (!exact || ((s_chosen[w][j >> 5] >> (j & 31)) & 1u))));
-      const uint64_t tm = __ballot(take);
-      const int pos = base + __popcll(tm & lt);
-      if (take && pos < max_kept) out[pos] = j;
-      base += __popcll(tm);
+    const uint32_t keep = above_m | band_m;
+    const int incl = wave_inclusive_scan(__popc(keep));
+    int pos = nf + incl - __popc(keep);
+    for (uint32_t x = keep; x; x &= x - 1u) {
+      if (pos < max_kept) out[pos] = j0 + __builtin_ctz(x);
+      ++pos;
     }
+    const int base = nf + __builtin_amdgcn_readlane(incl, 63);
     for (int p = base + lane; p < max_kept; p += 64) out[p] = -1;
     if (lane == 0) cnt[row] = base;
     return;
@@ -463,51 +542,40 @@ __global__ __launch_bounds__(64 * kSWaves, C > 18 ? 2 : 4) void band_select_kern
   }
   __builtin_amdgcn_wave_barrier();
   auto key_at = [&](int j) -> uint32_t { return (j >= nf && j < nkb) ? order_key(srow[j]) : 0u; };
-  uint32_t ekey[C];
-  float v[C];
+  // slot c of lane l = block l + 64 c (the row selector's layout)
+  uint32_t ekey[CL];
+  float v[CL];
 #pragma unroll
-  for (int c = 0; c < C; ++c) v[c] = srow[lane + 64 * c];
+  for (int c = 0; c < CL; ++c) v[c] = srow[lane + 64 * c];
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
+  for (int c = 0; c < CL; ++c) {
     const int j = lane + 64 * c;
     ekey[c] = static_cast<unsigned>(j - nf) < static_cast<unsigned>(nkb - nf) ? order_key(v[c]) : 0u;
   }
   __builtin_amdgcn_wave_barrier();
   // the keys are in registers, so the row's slice holds the candidate keys
-  const int n = select_row<C>(ekey, key_at, lane, nkb, nf, k, reinterpret_cast<uint32_t*>(srow), out,
-                              max_kept);
+  const int n = select_row<CL>(ekey, key_at, lane, nkb, nf, k, reinterpret_cast<uint32_t*>(srow), out,
+                               max_kept);
   if (lane == 0) cnt[row] = n;
 }
 
-// Resident one-wavefront workgroups of `kernel` on the current device.
-template <typename K>
-sparstar_status resident_waves(K kernel, int64_t& waves) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0) != hipSuccess ||
-      cus < 1 || per_cu < 1) {
-    set_error("sparstar_select_blocks_from_means: cannot query the device");
-    return SPARSTAR_ERR_HIP;
-  }
-  waves = static_cast<int64_t>(cus) * per_cu;
-  return SPARSTAR_OK;
-}
-
-// Workspace layout: screened scores [BH][nqb][ws_stride] float16, then the
-// squared norms of the key-block means [BH][nkb] float32 (256-byte aligned).
+// Workspace layout: screened scores [BH][nqb][ws_stride] float16 with
+// ws_stride = 128 * cstrips (cstrips = ceil(nkb / 128), CL = 2 cstrips keys
+// per lane), then the strip maxima of the squared key norms [BH][cstrips]
+// float32 (256-byte aligned).
 struct Layout {
-  int C, ws_stride;
-  int64_t kn2_off, total;
+  int cstrips, CL, ws_stride;
+  int64_t kmax_off, total;
 };
 
 Layout layout_of(int64_t BH, int64_t nqb, int64_t nkb) {
   auto up256 = [](int64_t x) { return (x + 255) / 256 * 256; };
   Layout L;
-  L.C = keys_per_lane(nkb);
-  L.ws_stride = 64 * (L.C > 0 ? L.C : 1);
-  L.kn2_off = up256(BH * nqb * L.ws_stride * 2);
-  L.total = L.kn2_off + BH * nkb * 4;
+  L.cstrips = static_cast<int>((nkb + kScrCols - 1) / kScrCols);
+  L.CL = 2 * L.cstrips;
+  L.ws_stride = kScrCols * L.cstrips;
+  L.kmax_off = up256(BH * nqb * L.ws_stride * 2);
+  L.total = L.kmax_off + BH * L.cstrips * 4;
   return L;
 }
 
@@ -520,7 +588,7 @@ int64_t fused_select_max_nkb() { return kMaxNkb; }
 // a caller workspace.  Each GPU the library runs on holds its own copy until
 // the process ends; every call on that GPU uses it, so calls that overlap in
 // time on one GPU race.  Nothing in it needs to start at zero (the screening
-// kernel writes every entry the band kernel reads for real blocks).
+// kernel writes every entry the band kernel reads).
 // ---------------------------------------------------------------------------
 constexpr int64_t kScratchBytes = int64_t(64) << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
@@ -573,24 +641,26 @@ sparstar_status launch_scores_select(const float* qbar, const float* kbar, int64
                                      hipStream_t s) {
   const Layout L = layout_of(BH, nqb, nkb);
   uint16_t* app = static_cast<uint16_t*>(workspace);
-  float* kn2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.kn2_off);
+  float* kmaxp = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.kmax_off);
   const int n = (int)nkb, nq = (int)nqb, f = (int)n_forced, kk = (int)k, mk = (int)max_kept;
 
-  // A. screening: exactly the resident wavefronts, items split evenly
-  const int64_t sstrips = (nqb + 16 * kScreenRowTiles - 1) / (16 * kScreenRowTiles);
-  const int64_t pairs = ((nkb + 15) / 16 + kScreenColTiles - 1) / kScreenColTiles;
-  const int64_t items = BH * sstrips * pairs;
-  int64_t waves = 0;
-  sparstar_status st = resident_waves(D == 128 ? screen_kernel<128> : screen_kernel<64>, waves);
-  if (st != SPARSTAR_OK) return st;
-  const dim3 sgrid(static_cast<uint32_t>(items < waves ? items : waves)), sblock(64);
+  // A. screening: one workgroup per 128 x 128 tile, dealt out per XCD
+  const int64_t rstrips = (nqb + kScrRows - 1) / kScrRows;
+  const int64_t tiles = BH * rstrips * L.cstrips;
+  if (tiles > 2147483647LL - kXcds) {
+    set_error("sparstar_select_blocks_from_means: grid too large");
+    return SPARSTAR_ERR_INVALID_ARGUMENT;
+  }
+  const int per_xcd = static_cast<int>((tiles + kXcds - 1) / kXcds);
+  const dim3 sgrid(static_cast<uint32_t>(per_xcd) * kXcds), sblock(64 * kScrWaves);
   if (D == 128)
-    screen_kernel<128><<<sgrid, sblock, 0, s>>>(qbar, kbar, nq, n, (int)sstrips, (int)pairs, items,
-                                                tau, L.ws_stride, app, kn2);
+    screen_kernel<128><<<sgrid, sblock, 0, s>>>(qbar, kbar, nq, n, f, (int)rstrips, L.cstrips,
+                                                (int)tiles, per_xcd, tau, L.ws_stride, app, kmaxp);
   else
-    screen_kernel<64><<<sgrid, sblock, 0, s>>>(qbar, kbar, nq, n, (int)sstrips, (int)pairs, items,
-                                               tau, L.ws_stride, app, kn2);
-  if ((st = check_launch("sparstar_select_blocks_from_means")) != SPARSTAR_OK) return st;
+    screen_kernel<64><<<sgrid, sblock, 0, s>>>(qbar, kbar, nq, n, f, (int)rstrips, L.cstrips,
+                                               (int)tiles, per_xcd, tau, L.ws_stride, app, kmaxp);
+  sparstar_status st = check_launch("sparstar_select_blocks_from_means");
+  if (st != SPARSTAR_OK) return st;
 
   // B. band selection, one wavefront per query block
   const int64_t rows = BH * nqb;
@@ -600,9 +670,9 @@ sparstar_status launch_scores_select(const float* qbar, const float* kbar, int64
     return SPARSTAR_ERR_INVALID_ARGUMENT;
   }
   // the exact route keeps one row of float32 scores per wavefront: every slot
-  // a lane reads (64 C of them) lies inside it, and it holds the selector's
+  // a lane reads (64 CL of them) lies inside it, and it holds the selector's
   // 128 candidate words
-  const int stride = 64 * L.C < 128 ? 128 : 64 * L.C;
+  const int stride = 64 * L.CL < 128 ? 128 : 64 * L.CL;
   const size_t lds = static_cast<size_t>(kSWaves) * stride * sizeof(float);
   const dim3 grid(static_cast<uint32_t>(wgs)), block(64 * kSWaves);
   hipError_t e = hipSuccess;
@@ -612,8 +682,8 @@ sparstar_status launch_scores_select(const float* qbar, const float* kbar, int64
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));  \
   if (e == hipSuccess)                                                                            \
     band_select_kernel<DD, CC><<<grid, block, lds, s>>>(qbar, kbar, rows, nq, n, tau, f, kk, app, \
-                                                        kn2, L.ws_stride, stride, kv_count,       \
-                                                        kv_index, mk);
+                                                        kmaxp, L.cstrips, L.ws_stride, stride,    \
+                                                        kv_count, kv_index, mk);
 #define SPARSTAR_BAND_CASE(CC)         \
   case CC:                             \
     if (D == 128) {                    \
@@ -622,8 +692,11 @@ sparstar_status launch_scores_select(const float* qbar, const float* kbar, int64
       SPARSTAR_BAND_CASE_D(64, CC)     \
     }                                  \
     break;
-  switch (L.C) {
-    SPARSTAR_FOR_EACH_C(SPARSTAR_BAND_CASE)
+  switch (L.CL) {
+    SPARSTAR_BAND_CASE(2) SPARSTAR_BAND_CASE(4) SPARSTAR_BAND_CASE(6) SPARSTAR_BAND_CASE(8)
+    SPARSTAR_BAND_CASE(10) SPARSTAR_BAND_CASE(12) SPARSTAR_BAND_CASE(14) SPARSTAR_BAND_CASE(16)
+    SPARSTAR_BAND_CASE(18) SPARSTAR_BAND_CASE(20) SPARSTAR_BAND_CASE(22) SPARSTAR_BAND_CASE(24)
+    SPARSTAR_BAND_CASE(26) SPARSTAR_BAND_CASE(28) SPARSTAR_BAND_CASE(30) SPARSTAR_BAND_CASE(32)
     default:
       set_error("sparstar_select_blocks_from_means: nkb > %lld is not supported",
                 (long long)fused_select_max_nkb());

@@ -162,7 +162,7 @@ __device__ __forceinline__ int select_row(const uint32_t* key, KeyAt key_at, int
 #define SPARSTAR_FOR_EACH_C(X) X(1) X(2) X(3) X(4) X(6) X(8) X(10) X(12) X(14) X(16) X(18) X(20) X(24) X(28) X(32)
 #define SPARSTAR_FOR_EACH_C_LARGE(X) X(40) X(48) X(56) X(64) X(72)
 
-int keys_per_lane(int64_t nkb) {
+inline int keys_per_lane(int64_t nkb) {
   const int64_t c = (nkb + 63) / 64;
   const int table[] = {1, 2, 3, 4, 6, 8, 10, 12, 14, 16, 18, 20, 24, 28, 32, 40, 48, 56, 64, 72};
   for (int t : table)

@@ -126,9 +126,10 @@ sparstar_status sparstar_select_blocks(const float* S, int64_t B, int64_t H, int
  * held in registers); larger nkb returns SPARSTAR_ERR_UNSUPPORTED.
  * workspace: caller-owned device memory of at least
  * sparstar_select_workspace_bytes(B, H, nqb, nkb) bytes, 256-byte aligned,
- * used as scratch (the screened scores as float16, nqb x ~nkb per head, and
- * the key-block norms); its contents before and after the call carry no
- * meaning.  Two calls in flight at once must not share a workspace.
+ * used as scratch (the screened scores as float16, nqb x 128 ceil(nkb / 128)
+ * per head, and the largest key-block norm of each strip of 128 blocks); its
+ * contents before and after the call carry no meaning.  Two calls in flight
+ * at once must not share a workspace.
  */
 sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float* kbar,
                                                   int64_t B, int64_t H, int64_t nqb, int64_t nkb,

@@ -136,8 +136,10 @@ def test_fused_select_validation():
     _err(call(ws_bytes=ws - 1), sp.ERR_INVALID_ARGUMENT, "workspace_bytes")
     big = sp.FUSED_MAX_NKB + 1
     _err(call(nkb=big, max_kept=big), sp.ERR_UNSUPPORTED, "nkb")
-    # workspace sizes: float16 screened scores (64 * ceil(nkb / 64) per row) + norms
-    assert sp.select_workspace_bytes(1, 16, 563, 1129) == 16 * 563 * 1152 * 2 + 16 * 1129 * 4
+    # workspace sizes: float16 screened scores (128 * ceil(nkb / 128) per row),
+    # then one float per (head, 128-block strip) of key norms, 256-byte aligned
+    assert sp.select_workspace_bytes(1, 16, 563, 1129) == 16 * 563 * 1152 * 2 + 16 * 9 * 4
+    assert sp.select_workspace_bytes(1, 1, 3, 129) == 3 * 256 * 2 + 2 * 4
     assert sp.select_workspace_bytes(1, 1, 4, 2049) == -1
     assert sp.select_workspace_bytes(0, 1, 4, 16) == -1
     # the largest supported row passes validation up to the launch (not made here)
