@@ -20,14 +20,18 @@
 //     +inf.  The largest squared norm of the key-block means of each
 //     128-block strip goes to the workspace too.
 //  B. band_select_kernel, one wavefront per query block (row): a rigorous
-//     bound E on |A_ij - F_ij| (A the stored value): the omitted split terms
-//     (<= 3.02 * 2^-16 |q_d k_d|), the float32 accumulation of 3 D products
-//     (gamma with u = 2^-23, whatever the hardware's internal rounding), the
-//     scaling, the float16 storage (2^-11 relative, 2^-25 absolute) and F's
-//     own rounding, the dot-product terms bounded by |qbar_i| max_j |kbar_j|.
-//     T = the k-th largest A (radix select on 16-bit order keys); blocks with
-//     A > T + 2E are kept and blocks with A < T - 2E dropped, each provably
-//     so; the blocks in between ("the band") are decided on their exact F_ij,
+//     bound |A_ij - F_ij| <= e(A_ij) = 1.001 (e1 + 6e-4 |A_ij|) (A the stored
+//     value).  e1 = 1.2e-4 |tau| |qbar_i| max_j |kbar_j| covers the omitted
+//     split terms (<= 3.02 * 2^-16 |q_d k_d|) and the float32 accumulation of
+//     3 D products (gamma with u = 2^-23, whatever the hardware's internal
+//     rounding), plus 1e-7 for float16 subnormals; 6e-4 |A| covers the
+//     scaling, the float16 storage (2^-11 relative) and F's own rounding.
+//     T = the k-th largest A (radix select on 16-bit order keys).  As
+//     a -+ 6.006e-4 |a| increase with a, the k blocks with the largest A
+//     have F >= T - e(T) and the others F <= T + e(T), so F's k-th largest
+//     lies in [T - e(T), T + e(T)]; blocks with A above hi (below lo), set so
+//     that F_ij is provably above (below) that interval, are kept (dropped);
+//     the blocks in between ("the band") are decided on their exact F_ij,
 //     keeping the best (k - #kept) by (F descending, index ascending).  The
 //     exact values come from the score kernel's own fp64 tile code
 //     (score_tile.hpp) with this row at its own position in its 16-row tile
@@ -113,7 +117,7 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-// Largest and smallest of an unsigned value over the 64 lanes.
+// Largest unsigned value over the 64 lanes.
 __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
   int x = static_cast<int>(v);
   x = static_cast<int>(max(static_cast<uint32_t>(x), static_cast<uint32_t>(dpp_i<0x111>(x, x))));
@@ -123,9 +127,6 @@ __device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
   x = static_cast<int>(max(static_cast<uint32_t>(x), static_cast<uint32_t>(dpp_i<0x142, 0xa>(x, x))));
   x = static_cast<int>(max(static_cast<uint32_t>(x), static_cast<uint32_t>(dpp_i<0x143, 0xc>(x, x))));
   return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
-}
-__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
-  return ~wave_max_u(~v);
 }
 
 // One level of a radix select from the top: hist[b] counts the candidates
@@ -345,7 +346,9 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
       }
     }
     // patch: 32 query rows x 64 keys of float16 (128 bytes), chunk ^ (row % 8);
-    // forced blocks and blocks past nkb become the sentinel
+    // forced blocks and blocks past nkb (only in the pairs that hold any)
+    // become the sentinel
+    const bool edge = c0 + 64 * p < nf || c0 + 64 * p + 64 > nkb;
     {
       const int r = lane % 32;
 #pragma unroll
@@ -356,10 +359,13 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
           uint32_t h[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            uint32_t b = __builtin_bit_cast(uint16_t, static_cast<_Float16>(tau * acc[u][4 * j + e]));
-            if ((b & 0x7c00u) == 0x7c00u) b = kNaN16;           // inf or NaN
-            const int jb = kb0 + e;
-            h[e] = (jb < nf || jb >= nkb) ? kSentinel16 : b;
+            const uint32_t b = __builtin_bit_cast(uint16_t, static_cast<_Float16>(tau * acc[u][4 * j + e]));
+            h[e] = (b & 0x7c00u) == 0x7c00u ? kNaN16 : b;       // inf or NaN
+          }
+          if (edge) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (kb0 + e < nf || kb0 + e >= nkb) h[e] = kSentinel16;
           }
           const int ch = 4 * u + j;
           *reinterpret_cast<u32x2*>(os + r * 128 + (ch ^ (r & 7)) * 16 + 8 * (lane / 32)) =
@@ -431,14 +437,13 @@ __global__ __launch_bounds__(64 * kSWaves, CL > 18 ? 2 : 4) void band_select_ker
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) qx[e] = qh[static_cast<int64_t>(i) * D + lane + 64 * e];
 
-  // order keys (0 = ineligible); the largest key and the smallest nonzero one
+  // order keys (0 = ineligible) and the largest of them
   uint32_t key[CL];
-  uint32_t kbig = 0u, ksmall_m1 = 0xffffu;
+  uint32_t kbig = 0u;
 #pragma unroll
   for (int s = 0; s < CL; ++s) {
     key[s] = key16((s & 1) ? (wv[s / 2] >> 16) : (wv[s / 2] & 0xffffu));
     kbig = max(kbig, key[s]);
-    ksmall_m1 = min(ksmall_m1, (key[s] - 1u) & 0xffffu);   // key 0 -> 0xffff
   }
   float qss = 0.f;
 #pragma unroll
@@ -449,14 +454,17 @@ __global__ __launch_bounds__(64 * kSWaves, CL > 18 ? 2 : 4) void band_select_ker
   uint32_t above_m = 0u, band_m = 0u;                // CL-bit masks of this lane's blocks
   bool exact = false;
   if (!full_exact && k > 0) {
-    const uint32_t ksmall = wave_min_u(ksmall_m1) + 1u;   // >= 0x0400: k > 0 eligible keys exist
-    const float amax = fmaxf(value_of_key16(kbig), -value_of_key16(ksmall));
     const float kmax = sqrtf(__uint_as_float(wave_max_u(__float_as_uint(kmx2)))) * 1.0001f;
     const float qn = sqrtf(wave_sum_f(qss)) * 1.0001f;
     const float t = value_of_key16(kth_largest16<CL>(key, k, lane, s_hist[w]));
-    const float E = 1.2e-4f * fabsf(tau) * qn * kmax + 6e-4f * amax + 1e-7f;
-    const float lo = t - 2.f * E, hi = t + 2.f * E;
-    if (!(E < INFINITY) || !(fabsf(lo) < INFINITY) || !(fabsf(hi) < INFINITY)) {
+    // |A_j - F_j| <= 1.001 (e1 + 6e-4 |A_j|) =: e(A_j); then F's k-th largest
+    // lies in [t - e(t), t + e(t)], and A_j > hi (A_j < lo) puts F_j above
+    // (below) that interval, because a -+ 6.006e-4 |a| increase with a
+    const float e1 = 1.2e-4f * fabsf(tau) * qn * kmax + 1e-7f;
+    const float X = t + 2.002f * e1 + 6.006e-4f * fabsf(t);
+    const float Y = t - 2.002f * e1 - 6.006e-4f * fabsf(t);
+    const float hi = X + 7e-4f * fabsf(X) + 1e-7f, lo = Y - 7e-4f * fabsf(Y) - 1e-7f;
+    if (!(fabsf(lo) < INFINITY) || !(fabsf(hi) < INFINITY)) {
       full_exact = true;
     } else {
       // keys of values > hi, and of values >= lo (klo >= 0x0400 > key 0)
@@ -495,12 +503,13 @@ __global__ __launch_bounds__(64 * kSWaves, CL > 18 ? 2 : 4) void band_select_ker
         }
         __builtin_amdgcn_wave_barrier();
         // keep the best `need` of the band: higher F first, then the lower index
+        // (lane e holds band block e; the others are broadcast from their lanes)
         const float fe = lane < m ? s_bandF[w][lane] : 0.f;
         const int ce = lane < m ? s_bandC[w][lane] : 0;
         int rank = 0;
         for (int e = 0; e < m; ++e) {
-          const float f2 = s_bandF[w][e];
-          const int c2 = s_bandC[w][e];
+          const float f2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fe), e));
+          const int c2 = __builtin_amdgcn_readlane(ce, e);
           rank += (f2 > fe || (f2 == fe && c2 < ce)) ? 1 : 0;
         }
         if (lane < m && rank < need) atomicOr(&s_chosen[w][ce / CL], 1u << (ce % CL));
