@@ -49,7 +49,11 @@ def attn_source_sha():
     for path in ATTN_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
-    h.update(" ".join(compile_flags()).encode())
+    # the flags name the include directory by absolute path; hash it relative
+    # to the repository so that a copy elsewhere gives the same key
+    from block_sparse_attention_head_amd import build as _build
+    flags = " ".join(compile_flags()).replace(os.path.abspath(_build.ROOT), "<root>")
+    h.update(flags.encode())
     return h.hexdigest()
 
 
@@ -384,18 +388,23 @@ def main():
                                           kv_index=idx),
                  lambda: sp.block_sparse_attn_fwd(q, k, v, cnt, idx, block=blk, out=o, lse=lse)]
 
-    def step(ev=None):
+    def step(ev=None, per_call=False):
+        """One scale.  ev: events recorded on the launch stream before the
+        first call, before the attention call and at the end (per_call: also
+        before every other call)."""
+        last = len(calls) - 1
         for i, c in enumerate(calls):
-            if ev: ev[i].record(stream)
+            if ev and (per_call or i == 0 or i == last):
+                ev[i].record(stream)
             c()
         if ev: ev[len(calls)].record(stream)
 
     def measure(cold, steps):
-        """ms per step and mean ms per call.  Cold: each step follows an
-        overwrite of 512 MiB (L2 and MALL hold none of its inputs) and is
-        timed on its own; warm: `steps` steps back to back between two
-        events.  Per-call times come from a second pass with an event before
-        and after every call on the launch stream."""
+        """ms per step and mean ms of the selection stage and of attention.
+        Cold: each step follows an overwrite of 512 MiB (L2 and MALL hold
+        none of its inputs) and is timed on its own; warm: `steps` steps back
+        to back between two events.  Stage times come from a second pass
+        with events only at the stage boundaries on the launch stream."""
         if cold:
             per = []
             for _ in range(steps):
@@ -416,16 +425,29 @@ def main():
             b.record(stream)
             torch.cuda.synchronize()
             ms = a.elapsed_time(b) / steps
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-               for _ in range(steps)]
+        n = len(calls)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
         for e in evs:
             if cold:
                 flush.fill_(0)
             step(e)
         torch.cuda.synchronize()
-        per_call = {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-                    for i, n in enumerate(names)}
-        return ms, per_call
+        stages = {"selection": float(np.mean([e[0].elapsed_time(e[n - 1]) for e in evs])),
+                  "attn": float(np.mean([e[n - 1].elapsed_time(e[n]) for e in evs]))}
+        return ms, stages
+
+    def breakdown(cold, steps):
+        """Mean ms per selection call, an event before and after every call
+        (the events themselves add a few microseconds per call)."""
+        n = len(calls)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+        for e in evs:
+            if cold:
+                flush.fill_(0)
+            step(e, per_call=True)
+        torch.cuda.synchronize()
+        return {nm: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+                for i, nm in enumerate(names[:-1])}
 
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -435,6 +457,7 @@ def main():
     primary_cold = not args.warm
     log(f"[bench] timing {args.steps} steps ({'cold' if primary_cold else 'warm'} cache)")
     ms_per_step, stage_ms = measure(primary_cold, args.steps)
+    calls_ms = breakdown(primary_cold, min(args.steps, 10))
 
     graph_ms = None
     if args.graph:
@@ -460,7 +483,7 @@ def main():
     other_steps = min(args.steps, 10)
     log(f"[bench] {'warm' if primary_cold else 'cold'}-cache pass ({other_steps} steps)")
     o_ms, o_stage = measure(not primary_cold, other_steps)
-    o_sel = sum(o_stage[n] for n in names[:-1])
+    o_sel = o_stage["selection"]
     other = {"cache": "warm" if primary_cold else "cold",
              "ms_per_step": round(o_ms, 4),
              "selection_us": round(o_sel * 1e3, 2), "attn_us": round(o_stage["attn"] * 1e3, 2),
@@ -474,7 +497,7 @@ def main():
     flops = selected_flops(kv_count, kv_index, w.Nq, w.Nk, D, blk)
     attn_tflops = flops / (stage_ms["attn"] * 1e-3) / 1e12
     value = flops / (ms_per_step * 1e-3) / 1e12
-    sel_ms = sum(stage_ms[n] for n in names[:-1])
+    sel_ms = stage_ms["selection"]
     sbytes = stage_bytes(w, kept, nqb, nkb)
     dense_flops = 4 * D * w.Nq * w.Nk * B * H
     traffic = traffic_for_attention(w.name)
@@ -516,7 +539,8 @@ def main():
         "diagnostics": diag,
         "other_cache": other,
         "stages": {
-            **{f"{n}_us": round(stage_ms[n] * 1e3, 2) for n in names},
+            "attn_us": round(stage_ms["attn"] * 1e3, 2),
+            "selection_calls_us": {n: round(calls_ms[n] * 1e3, 2) for n in names[:-1]},
             "attn_tflops": round(attn_tflops, 2),
             "selection_us": round(sel_ms * 1e3, 2),
             "selection_alg_bytes": sbytes,
@@ -525,7 +549,7 @@ def main():
             "selection_share_of_scale": round(sel_ms / ms_per_step, 4),
             "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
             "means_gbps": round(B * H * (w.Nq + w.Nk) * D * (2 if w.dtype == "bf16" else 4)
-                                / ((stage_ms["means_q"] + stage_ms["means_k"]) * 1e-3) / 1e9, 1),
+                                / ((calls_ms["means_q"] + calls_ms["means_k"]) * 1e-3) / 1e9, 1),
         },
     }
     print(json.dumps(rec), flush=True)
