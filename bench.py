@@ -313,6 +313,9 @@ def main():
     ap.add_argument("--two-step", action="store_true",
                     help="scores (float32 S in HBM) then selection, instead of the screened "
                          "route (sparstar_select_blocks_from_means, the same selection)")
+    ap.add_argument("--from-means", action="store_true",
+                    help="run the selection stage as three calls (means of Q, means of K, "
+                         "screened selection) instead of one call from Q and K")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step recorded as one HIP graph and replayed")
     ap.add_argument("--no-diagnostics", action="store_true",
@@ -371,7 +374,13 @@ def main():
     stream = torch.cuda.current_stream()
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
-    if fused:
+    if fused and not args.from_means:
+        names = ["select_from_qk", "attn"]
+        calls = [lambda: sp.select_blocks_from_qk(q, k, F, w.density, block=blk, max_kept=kept,
+                                                  qbar=qbar, kbar=kbar, kv_count=cnt,
+                                                  kv_index=idx, workspace=ws),
+                 lambda: sp.block_sparse_attn_fwd(q, k, v, cnt, idx, block=blk, out=o, lse=lse)]
+    elif fused:
         names = ["means_q", "means_k", "screened_select", "attn"]
         calls = [lambda: sp.block_means(q, blk, out=qbar),
                  lambda: sp.block_means(k, blk, out=kbar),
@@ -531,7 +540,9 @@ def main():
         "config": {**w.describe(), "block": blk, "kept_blocks": kept, "n_forced_blocks": F,
                    "selected_tflop": flops / 1e12, "dense_tflop": dense_flops / 1e12,
                    "cache": "cold" if primary_cold else "warm",
-                   "score_select": "screened" if fused else "two-step"},
+                   "score_select": ("screened, one call from Q and K"
+                                    if fused and not args.from_means else
+                                    "screened from the means" if fused else "two-step")},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
@@ -548,8 +559,9 @@ def main():
             "selection_frac_hbm": round(sbytes / (sel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
             "selection_share_of_scale": round(sel_ms / ms_per_step, 4),
             "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
-            "means_gbps": round(B * H * (w.Nq + w.Nk) * D * (2 if w.dtype == "bf16" else 4)
-                                / ((calls_ms["means_q"] + calls_ms["means_k"]) * 1e-3) / 1e9, 1),
+            "means_gbps": (round(B * H * (w.Nq + w.Nk) * D * (2 if w.dtype == "bf16" else 4)
+                                 / ((calls_ms["means_q"] + calls_ms["means_k"]) * 1e-3) / 1e9, 1)
+                           if "means_q" in calls_ms else None),
         },
     }
     print(json.dumps(rec), flush=True)

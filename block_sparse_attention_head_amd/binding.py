@@ -24,6 +24,9 @@ _SIGNATURES = {
     "sparstar_select_blocks_from_means": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _i64,
                                                          _f64, _vp, _vp, _i64, _vp, _i64, _vp]),
     "sparstar_select_workspace_bytes": (_i64, [_i64, _i64, _i64, _i64]),
+    "sparstar_select_blocks_from_qk": (ctypes.c_int, [_vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
+                                                      _i64, _f32, _i64, _f64, _vp, _vp, _vp, _vp, _i64,
+                                                      _vp, _i64, _vp]),
     "sparstar_select_blocks_from_means_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
                                                                  _i64, _f64, _vp, _vp, _i64, _vp]),
     "sparstar_block_sparse_attn_fwd": (ctypes.c_int, [_vp, _vp, _vp, ctypes.c_int, _i64, _i64, _i64, _i64,
@@ -229,6 +232,39 @@ def select_blocks_from_means(qbar, kbar, n_forced_blocks, density, tau=None, max
     return kv_count, kv_index
 
 
+def select_blocks_from_qk(q, k, n_forced_blocks, density, block=BLOCK, tau=None, max_kept=None,
+                          qbar=None, kbar=None, kv_count=None, kv_index=None, workspace=None,
+                          stream=None):
+    """The whole selection stage from q [B,H,Nq,D] and k [B,H,Nk,D] (same
+    dtype) in one library call: block means of both, then
+    select_blocks_from_means on them.  Returns (kv_count, kv_index, qbar, kbar)."""
+    torch = _torch()
+    B, H, Nq, D = q.shape
+    Nk = k.shape[2]
+    _expect(k, "k", (B, H, Nk, D), q.dtype)
+    nqb, nkb = -(-Nq // block), -(-Nk // block)
+    if qbar is None:
+        qbar = torch.empty((B, H, nqb, D), dtype=torch.float32, device=q.device)
+    if kbar is None:
+        kbar = torch.empty((B, H, nkb, D), dtype=torch.float32, device=q.device)
+    _expect(qbar, "qbar", (B, H, nqb, D), torch.float32)
+    _expect(kbar, "kbar", (B, H, nkb, D), torch.float32)
+    if tau is None:
+        tau = 1.0 / math.sqrt(D)
+    max_kept, kv_count, kv_index = _selection_buffers((B, H, nqb), n_forced_blocks, density, nkb,
+                                                      max_kept, kv_count, kv_index, q.device)
+    if workspace is None:
+        workspace = select_workspace(B, H, nqb, nkb, q.device)
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1:
+        raise TypeError("workspace must be a 1-D uint8 tensor")
+    _check(lib().sparstar_select_blocks_from_qk(
+        _dev(q, "q"), _dev(k, "k"), _dtype_code(q), B, H, Nq, Nk, D, block, tau, n_forced_blocks,
+        density, _dev(qbar, "qbar"), _dev(kbar, "kbar"), _dev(kv_count, "kv_count"),
+        _dev(kv_index, "kv_index"), max_kept, _dev(workspace, "workspace"), workspace.numel(),
+        _stream(stream)))
+    return kv_count, kv_index, qbar, kbar
+
+
 def select_blocks_from_means_noalloc(qbar, kbar, n_forced_blocks, density, tau=None,
                                      max_kept=None, kv_count=None, kv_index=None, stream=None):
     """select_blocks_from_means without a workspace: the library's own device
@@ -349,16 +385,18 @@ def sparse_attention(q, k, v, n_forced_tokens, density, block=BLOCK, return_all=
                      fused=False, stream=None):
     """The whole path for one scale: means -> scores -> selection -> attention.
 
-    With ``fused`` (and nkb <= FUSED_MAX_NKB) scores and selection run as one
-    launch and S is never materialised (``return_all`` then gives S = None).
+    With ``fused`` (and nkb <= FUSED_MAX_NKB) the selection stage is one
+    select_blocks_from_qk call (screened scores) and S is never materialised
+    (``return_all`` then gives S = None).
     """
-    qbar = block_means(q, block, stream=stream)
-    kbar = block_means(k, block, stream=stream)
     F = forced_blocks(n_forced_tokens, block)
-    if fused and kbar.shape[2] <= FUSED_MAX_NKB:
+    if fused and -(-k.shape[2] // block) <= FUSED_MAX_NKB:
         S = None
-        kv_count, kv_index = select_blocks_from_means(qbar, kbar, F, density, stream=stream)
+        kv_count, kv_index, qbar, kbar = select_blocks_from_qk(q, k, F, density, block=block,
+                                                               stream=stream)
     else:
+        qbar = block_means(q, block, stream=stream)
+        kbar = block_means(k, block, stream=stream)
         S = block_scores(qbar, kbar, stream=stream)
         kv_count, kv_index = select_blocks(S, F, density, stream=stream)
     o, lse = block_sparse_attn_fwd(q, k, v, kv_count, kv_index, block=block, stream=stream)

@@ -75,7 +75,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 }  // namespace
 
 namespace {
-// Arguments of the screened score + selection route (both entry points).
+// Arguments of the screened score + selection route (every entry point to it).
 sparstar_status check_select_from_means(const char* fn, const float* qbar, const float* kbar,
                                         int64_t B, int64_t H, int64_t nqb, int64_t nkb,
                                         int64_t D, float tau, int64_t n_forced_blocks,
@@ -107,11 +107,26 @@ sparstar_status check_select_from_means(const char* fn, const float* qbar, const
   *kept_out = kept;
   return SPARSTAR_OK;
 }
+
+// The caller workspace of the screened route: present, 256-byte aligned, large enough.
+sparstar_status check_workspace(const char* fn, const void* workspace, int64_t workspace_bytes,
+                                int64_t BH, int64_t nqb, int64_t nkb) {
+  if (!workspace) return invalid(fn, "null pointer");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return invalid(fn, "workspace must be 256-byte aligned");
+  const int64_t need = select_workspace_bytes(BH, nqb, nkb);
+  if (workspace_bytes < need) {
+    set_error("%s: workspace_bytes (%lld) < %lld (sparstar_select_workspace_bytes)", fn,
+              (long long)workspace_bytes, (long long)need);
+    return SPARSTAR_ERR_INVALID_ARGUMENT;
+  }
+  return SPARSTAR_OK;
+}
 }  // namespace
 
 extern "C" {
 
-int32_t sparstar_version(void) { return 10300; }
+int32_t sparstar_version(void) { return 10400; }
 
 const char* sparstar_last_error(void) { return g_err; }
 
@@ -203,18 +218,43 @@ sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float
                                                n_forced_blocks, density, kv_count, kv_index,
                                                max_kept, &kept);
   if (st != SPARSTAR_OK) return st;
-  if (!workspace) return invalid(fn, "null pointer");
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return invalid(fn, "workspace must be 256-byte aligned");
-  const int64_t need = select_workspace_bytes(B * H, nqb, nkb);
-  if (workspace_bytes < need) {
-    set_error("%s: workspace_bytes (%lld) < %lld (sparstar_select_workspace_bytes)", fn,
-              (long long)workspace_bytes, (long long)need);
-    return SPARSTAR_ERR_INVALID_ARGUMENT;
-  }
+  if ((st = check_workspace(fn, workspace, workspace_bytes, B * H, nqb, nkb)) != SPARSTAR_OK)
+    return st;
   return launch_scores_select(qbar, kbar, B * H, nqb, nkb, D, tau, n_forced_blocks,
                               kept - n_forced_blocks, kv_count, kv_index, max_kept, workspace,
                               static_cast<hipStream_t>(stream));
+}
+
+sparstar_status sparstar_select_blocks_from_qk(const void* q, const void* k, sparstar_dtype dtype,
+                                               int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                               int64_t D, int64_t block, float tau,
+                                               int64_t n_forced_blocks, double density,
+                                               float* qbar, float* kbar, int32_t* kv_count,
+                                               int32_t* kv_index, int64_t max_kept,
+                                               void* workspace, int64_t workspace_bytes,
+                                               void* stream) {
+  const char* fn = "sparstar_select_blocks_from_qk";
+  clear_error();
+  if (!q || !k) return invalid(fn, "null pointer");
+  if (!aligned16(q) || !aligned16(k)) return invalid(fn, "q and k must be 16-byte aligned");
+  if (dtype != SPARSTAR_FP32 && dtype != SPARSTAR_BF16) return invalid(fn, "unknown dtype");
+  sparstar_status st = check_bhnd(fn, B, H, Nq, D);
+  if (st != SPARSTAR_OK) return st;
+  if ((st = check_bhnd(fn, B, H, Nk, D)) != SPARSTAR_OK) return st;
+  if ((st = check_block(fn, block)) != SPARSTAR_OK) return st;
+  const int64_t nqb = (Nq + block - 1) / block, nkb = (Nk + block - 1) / block;
+  int64_t kept = 0;
+  if ((st = check_select_from_means(fn, qbar, kbar, B, H, nqb, nkb, D, tau, n_forced_blocks,
+                                    density, kv_count, kv_index, max_kept, &kept)) != SPARSTAR_OK)
+    return st;
+  if ((st = check_workspace(fn, workspace, workspace_bytes, B * H, nqb, nkb)) != SPARSTAR_OK)
+    return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  // two launches: one launch over both tensors measured slower on MI355X
+  if ((st = launch_block_means(q, dtype, B * H, Nq, D, block, qbar, s)) != SPARSTAR_OK) return st;
+  if ((st = launch_block_means(k, dtype, B * H, Nk, D, block, kbar, s)) != SPARSTAR_OK) return st;
+  return launch_scores_select(qbar, kbar, B * H, nqb, nkb, D, tau, n_forced_blocks,
+                              kept - n_forced_blocks, kv_count, kv_index, max_kept, workspace, s);
 }
 
 sparstar_status sparstar_select_blocks_from_means_noalloc(const float* qbar, const float* kbar,

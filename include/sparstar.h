@@ -143,6 +143,32 @@ sparstar_status sparstar_select_blocks_from_means(const float* qbar, const float
 int64_t sparstar_select_workspace_bytes(int64_t B, int64_t H, int64_t nqb, int64_t nkb);
 
 /*
+ * The whole selection stage of one scale from Q and K ("What carries the
+ * argument": block means, Eq. 2 scores, clip-aware joint Top-K): the block
+ * means of q and of k, as sparstar_block_means computes them, into qbar and
+ * kbar (caller buffers, left holding the means), then the selection of
+ * sparstar_select_blocks_from_means on them, with the same workspace rules:
+ * one call for the stage, four kernel launches.  The result equals
+ * sparstar_block_means(q), sparstar_block_means(k) and
+ * sparstar_select_blocks_from_means(qbar, kbar, ...) bit for bit.
+ *   q [B,H,Nq,D] and k [B,H,Nk,D] of `dtype`, 16-byte aligned; block as for
+ *   sparstar_block_means; qbar [B,H,ceil(Nq/block),D] and
+ *   kbar [B,H,ceil(Nk/block),D] float32; kv_count [B,H,nqb] and
+ *   kv_index [B,H,nqb,max_kept] with nqb = ceil(Nq/block).
+ * Requirements: those of sparstar_block_means for q and k and of
+ * sparstar_select_blocks_from_means with nkb = ceil(Nk/block); every check is
+ * made before anything is enqueued.
+ */
+sparstar_status sparstar_select_blocks_from_qk(const void* q, const void* k, sparstar_dtype dtype,
+                                               int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                               int64_t D, int64_t block, float tau,
+                                               int64_t n_forced_blocks, double density,
+                                               float* qbar, float* kbar, int32_t* kv_count,
+                                               int32_t* kv_index, int64_t max_kept,
+                                               void* workspace, int64_t workspace_bytes,
+                                               void* stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * operation, arguments, result and requirements as

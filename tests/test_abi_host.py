@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_helpers():
-    assert sp.version() == 10300
+    assert sp.version() == 10400
     assert sp.forced_blocks(0) == 0
     assert sp.forced_blocks(1) == 1
     assert sp.forced_blocks(128) == 1
@@ -144,6 +144,43 @@ def test_fused_select_validation():
     assert sp.select_workspace_bytes(0, 1, 4, 16) == -1
     # the largest supported row passes validation up to the launch (not made here)
     assert sp.FUSED_MAX_NKB == 2048
+
+
+def test_select_from_qk_validation():
+    """The whole-stage entry point checks the means' and the selection's
+    arguments, and the workspace, before anything is enqueued."""
+    f = _lib().sparstar_select_blocks_from_qk
+    ws = sp.select_workspace_bytes(1, 1, 4, 16)
+    BF = sp.BF16
+    ok = [FAKE, FAKE, BF, 1, 1, 500, 2000, 128, 128, 0.088, 1, 0.25, FAKE, FAKE, FAKE, FAKE, 5, FAKE,
+          ws, NULL]
+
+    def call(**kw):
+        a = list(ok)
+        pos = {"q": 0, "k": 1, "dtype": 2, "Nq": 5, "Nk": 6, "D": 7, "block": 8, "tau": 9, "F": 10,
+               "density": 11, "qbar": 12, "cnt": 14, "max_kept": 16, "ws": 17, "ws_bytes": 18}
+        for k, v in kw.items():
+            a[pos[k]] = v
+        return f(*a)
+
+    _err(call(q=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(k=ctypes.c_void_p(4100)), sp.ERR_INVALID_ARGUMENT, "aligned")
+    _err(call(dtype=7), sp.ERR_INVALID_ARGUMENT, "dtype")
+    _err(call(Nq=0), sp.ERR_INVALID_ARGUMENT, "sequence length")
+    _err(call(Nk=0), sp.ERR_INVALID_ARGUMENT, "sequence length")
+    _err(call(D=96), sp.ERR_UNSUPPORTED, "D must be")
+    _err(call(block=48), sp.ERR_UNSUPPORTED, "block")
+    _err(call(qbar=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(cnt=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(tau=float("nan")), sp.ERR_INVALID_ARGUMENT, "tau")
+    _err(call(F=17), sp.ERR_INVALID_ARGUMENT, "n_forced")
+    _err(call(density=-0.5), sp.ERR_INVALID_ARGUMENT, "density")
+    _err(call(max_kept=4), sp.ERR_INVALID_ARGUMENT, "max_kept")
+    # nkb = ceil(Nk / block): 2049 blocks exceed the screened route
+    _err(call(Nk=2049 * 128, max_kept=2049), sp.ERR_UNSUPPORTED, "nkb")
+    _err(call(ws=NULL), sp.ERR_INVALID_ARGUMENT, "null")
+    _err(call(ws=ctypes.c_void_p(4096 + 64)), sp.ERR_INVALID_ARGUMENT, "256-byte")
+    _err(call(ws_bytes=ws - 1), sp.ERR_INVALID_ARGUMENT, "workspace_bytes")
 
 
 def test_noalloc_validation():

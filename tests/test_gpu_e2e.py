@@ -52,7 +52,13 @@ def test_workload(cid, w):
         f_cnt, f_idx = sp.select_blocks_from_means(out["qbar"], out["kbar"], F, w.density)
         assert np.array_equal(f_cnt.cpu().numpy(), g_cnt)
         assert np.array_equal(f_idx.cpu().numpy(), g_idx)
-        log("  fused scores + selection: identical")
+        # and the whole stage from Q and K in one call
+        c3, i3, qb3, kb3 = sp.select_blocks_from_qk(q, k, F, w.density)
+        assert torch.equal(qb3, out["qbar"]) and torch.equal(kb3, out["kbar"])
+        assert np.array_equal(c3.cpu().numpy(), g_cnt)
+        assert np.array_equal(i3.cpu().numpy(), g_idx)
+        del c3, i3, qb3, kb3
+        log("  screened scores + selection, from the means and from Q and K: identical")
     o_gpu = out["o"]
     lse_gpu = out["lse"].cpu().numpy().astype(np.float64)
     del q, k, v, out

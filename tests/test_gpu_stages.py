@@ -170,6 +170,33 @@ def test_fused_select_repeated_calls_share_nothing():
         check_selection(ref_S, 4, 0.1, c.cpu().numpy(), i.cpu().numpy())
 
 
+QK_CASES = [
+    # dtype, D, block, Nq, Nk, F, density
+    ("bf16", 128, 128, 1000, 3000, 4, 0.25), ("fp32", 64, 64, 333, 2049, 0, 0.5),
+    ("bf16", 64, 32, 129, 4500, 2, 0.125), ("fp32", 128, 128, 1, 1, 0, 1.0),
+    ("bf16", 128, 128, 5000, 131000, 4, 0.09375), ("bf16", 128, 64, 777, 20000, 40, 0.0),
+]
+
+
+@pytest.mark.parametrize("dtype,D,block,Nq,Nk,F,density", QK_CASES)
+def test_select_from_qk_matches_the_separate_calls(dtype, D, block, Nq, Nk, F, density):
+    """One call for the whole selection stage (means of Q and K, then the
+    screened route) equals the means calls and select_blocks_from_means bit
+    for bit, means included."""
+    log(f"select from qk dtype={dtype} D={D} block={block} Nq={Nq} Nk={Nk} F={F} density={density}")
+    B, H = 1, 2
+    q = to_dev(_rand((B, H, Nq, D), dtype, seed=Nq + 3, offset=0.1), dtype)
+    k = to_dev(_rand((B, H, Nk, D), dtype, seed=Nk + 5, offset=0.2), dtype)
+    c1, i1, qb1, kb1 = sp.select_blocks_from_qk(q, k, F, density, block=block)
+    qb2, kb2 = sp.block_means(q, block), sp.block_means(k, block)
+    c2, i2 = sp.select_blocks_from_means(qb2, kb2, F, density)
+    assert torch.equal(qb1, qb2) and torch.equal(kb1, kb2)
+    assert torch.equal(c1, c2) and torch.equal(i1, i2)
+    # and the selection is the oracle's on the kernel's own means
+    S = oracle.block_scores(to_f64(qb1), to_f64(kb1))
+    check_selection(S, F, density, c1.cpu().numpy(), i1.cpu().numpy())
+
+
 # ---------------------------------------------------------------- attention
 def _attn_case(dtype, D, Nq, Nk, density, F_tokens, seed):
     rng = np.random.default_rng(seed)
