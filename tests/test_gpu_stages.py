@@ -383,3 +383,64 @@ def test_scale_captured_in_a_graph():
             assert torch.equal(t, eager[n]), (rep, n)
         scale()                             # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("route", ["from_qk", "noalloc"])
+def test_screened_scale_captured_in_a_graph(route):
+    """The scale on the screened route recorded as one HIP graph: the
+    whole-stage call with a caller workspace, or the means and the
+    allocation-free selection (the entry point meant for capture); every
+    replay equals the eager result bit for bit, with eager work between."""
+    (q, k, v), _, res = _attn_case("bf16", 128, 1100, 2600, 0.1875, 300, seed=12)
+    qd, kd, vd = (to_dev(a, "bf16") for a in (q, k, v))
+    B, H, Nq, D = qd.shape
+    nqb, nkb = -(-Nq // 128), -(-kd.shape[2] // 128)
+    F = sp.forced_blocks(300)
+    kept = sp.kept_blocks(nkb, F, 0.1875)
+    f32, i32, dev = torch.float32, torch.int32, qd.device
+    bufs = {"qbar": torch.empty((B, H, nqb, D), dtype=f32, device=dev),
+            "kbar": torch.empty((B, H, nkb, D), dtype=f32, device=dev),
+            "cnt": torch.empty((B, H, nqb), dtype=i32, device=dev),
+            "idx": torch.empty((B, H, nqb, kept), dtype=i32, device=dev),
+            "o": torch.empty_like(qd), "lse": torch.empty((B, H, Nq), dtype=f32, device=dev)}
+    ws = sp.select_workspace(B, H, nqb, nkb, dev)
+
+    def scale():
+        if route == "from_qk":
+            sp.select_blocks_from_qk(qd, kd, F, 0.1875, max_kept=kept, qbar=bufs["qbar"],
+                                     kbar=bufs["kbar"], kv_count=bufs["cnt"],
+                                     kv_index=bufs["idx"], workspace=ws)
+        else:
+            sp.block_means(qd, out=bufs["qbar"])
+            sp.block_means(kd, out=bufs["kbar"])
+            sp.select_blocks_from_means_noalloc(bufs["qbar"], bufs["kbar"], F, 0.1875,
+                                                max_kept=kept, kv_count=bufs["cnt"],
+                                                kv_index=bufs["idx"])
+        sp.block_sparse_attn_fwd(qd, kd, vd, bufs["cnt"], bufs["idx"], out=bufs["o"],
+                                 lse=bufs["lse"])
+
+    scale()
+    torch.cuda.synchronize()
+    eager = {n: t.clone() for n, t in bufs.items()}
+    # the screened route selects what the two-call route selects
+    c2, i2 = sp.select_blocks(sp.block_scores(eager["qbar"], eager["kbar"]), F, 0.1875,
+                              max_kept=kept)
+    assert torch.equal(c2, eager["cnt"]) and torch.equal(i2, eager["idx"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm the capture stream once
+        scale()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        scale()
+    for rep in range(3):
+        for t in bufs.values():
+            t.zero_()                       # replays must rewrite everything
+        ws.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in bufs.items():
+            assert torch.equal(t, eager[n]), (route, rep, n)
+        scale()                             # eager work between replays
+        torch.cuda.synchronize()
