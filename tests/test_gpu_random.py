@@ -38,9 +38,16 @@ def test_random_shape(seed):
     k += np.repeat(rng.standard_normal((B, H, -(-Nk // block), D), dtype=np.float32), block, axis=2)[:, :, :Nk]
     if dtype == "bf16":
         q, k, v = bf16_bits_from_f32(q), bf16_bits_from_f32(k), bf16_bits_from_f32(v)
-    res = sp.sparse_attention(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), n_forced, density,
-                              block=block, return_all=True)
+    q_t, k_t, v_t = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    res = sp.sparse_attention(q_t, k_t, v_t, n_forced, density, block=block, return_all=True)
     g_cnt, g_idx = res["kv_count"].cpu().numpy(), res["kv_index"].cpu().numpy()
+    # the screened route (one call from Q and K) selects exactly the same blocks
+    F_gpu = sp.forced_blocks(n_forced, block)
+    c_s, i_s, qb_s, kb_s = sp.select_blocks_from_qk(q_t, k_t, F_gpu, density, block=block)
+    assert np.array_equal(c_s.cpu().numpy(), g_cnt), f"seed {seed}: screened counts"
+    assert np.array_equal(i_s.cpu().numpy(), g_idx), f"seed {seed}: screened selection"
+    assert np.array_equal(qb_s.cpu().numpy(), res["qbar"].cpu().numpy())
+    assert np.array_equal(kb_s.cpu().numpy(), res["kbar"].cpu().numpy())
     qd, kd, vd = (oracle.decode(a, dtype) for a in (q, k, v))
     S = oracle.block_scores(oracle.block_means(qd, block), oracle.block_means(kd, block))
     F = oracle.forced_blocks(n_forced, block)
