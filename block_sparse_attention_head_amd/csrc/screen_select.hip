@@ -344,6 +344,16 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl[ks], a_hi[ks], acc[u], 0, 0, 0);
         acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh[ks], a_lo[ks], acc[u], 0, 0, 0);
       }
+      // the LDS reads two k-steps ahead of the MFMAs that use them (left
+      // alone the compiler reads each k-step just before its MFMAs and every
+      // third MFMA waits out the LDS latency); 0x100 = LDS reads, 0x008 = MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int x = 0; x < KS - 2; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     }
     // patch: 32 query rows x 64 keys of float16 (128 bytes), chunk ^ (row % 8);
     // forced blocks and blocks past nkb (only in the pairs that hold any)
