@@ -51,7 +51,10 @@
 namespace sparstar {
 namespace {
 
-constexpr int kSWaves = 4;       // wavefronts (rows) per band-selection workgroup
+// wavefronts (rows) per band-selection workgroup: one, so that a slot frees as
+// soon as its row is done (rows differ widely in work: a band decided on exact
+// scores takes an fp64 tile; four-row workgroups measured 2 us slower at 72k)
+constexpr int kSWaves = 1;
 constexpr int kBandCap = 48;     // band blocks per row decided on exact scores
 constexpr int kMaxNkb = 2048;    // key blocks per row (a row lives in registers)
 constexpr uint32_t kSentinel16 = 0xffffu;   // float16 bits whose order key is 0
@@ -400,8 +403,7 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
 // ---------------------------------------------------------------------------
 // B. band selection
 // ---------------------------------------------------------------------------
-// One wavefront per query block (row), kSWaves independent rows per
-// workgroup.  Lane l owns the CL consecutive blocks CL l .. CL l + CL - 1 of
+// One wavefront per query block (row), one row per workgroup.  Lane l owns the CL consecutive blocks CL l .. CL l + CL - 1 of
 // the row (keys in registers, sets of them as CL-bit masks), so counts and
 // the ascending output need one prefix sum over lanes, not one per slot.
 // The exact scores of the band come from fp64 tiles laid out as the score
@@ -409,7 +411,7 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
 // tile (this row at its own position), the B operand holds band blocks; only
 // this row's results are kept.
 template <int D, int CL>
-__global__ __launch_bounds__(64 * kSWaves, CL > 18 ? 2 : 4) void band_select_kernel(
+__global__ __launch_bounds__(64 * kSWaves) void band_select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t rows, int nqb, int nkb,
     float tau, int nf, int k, const uint16_t* __restrict__ app, const float* __restrict__ kmaxp,
     int cstrips, int ws_stride, int stride, int32_t* __restrict__ cnt, int32_t* __restrict__ idx,
