@@ -68,4 +68,32 @@ __device__ __forceinline__ void score_tiles16x2(const f32x4 (&qv)[D / 16], const
   }
 }
 
+// One row of q against 16 key columns, for a caller that needs a single row:
+// v_mfma_f64_4x4x4f64 (four blocks of 4 x 4, K = 4) spends a quarter of the
+// matrix-core cycles of a 16 x 16 tile on it.  Lane layout (gfx950): A lane
+// i + 4 b + 16 k = (row i, k) of block b, B lane j + 4 b + 16 k = (k, column
+// j) of block b, result lane j + 4 b + 16 i = (row i, column j) of block b.
+// Every lane passes the same row's slices (qv from the row, offset by
+// 4 * (lane / 16) as for score_tile16) and kv from key column 4 b + j =
+// lane % 16, so block b holds columns 4 b .. 4 b + 3 in all four rows and
+// lane c < 16 receives the sum for column c.  The dimension groups and their
+// order are score_tile16's (k-step e of chunk c: dimension 16 c + 4 k + e);
+// each step adds a four-product group to the running float64 sum, and the
+// two instructions give the same bits for it (checked by a GPU test on
+// random, cancelling and wide-range operands).
+template <int D>
+__device__ __forceinline__ double score_row16(const f32x4 (&qv)[D / 16], const f32x4 (&kv)[D / 16]) {
+  double acc = 0.0;
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) {
+    f32x4 q = qv[c];
+    asm volatile("" : "+v"(q));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f64_4x4x4f64(static_cast<double>(q[e]),
+                                               static_cast<double>(kv[c][e]), acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 }  // namespace sparstar

@@ -33,10 +33,9 @@
 //     that F_ij is provably above (below) that interval, are kept (dropped);
 //     the blocks in between ("the band") are decided on their exact F_ij,
 //     keeping the best (k - #kept) by (F descending, index ascending).  The
-//     exact values come from the score kernel's own fp64 tile code
-//     (score_tile.hpp) with this row at its own position in its 16-row tile
-//     and the same operations in the same order, hence the same float32
-//     values.  A band no larger than what it must supply needs no exact
+//     exact values are the score kernel's fp64 sums (score_tile.hpp): the
+//     same dimension groups in the same order, on the one-row 4 x 4 x 4
+//     form of its matrix-core step, hence the same float32 values.  A band no larger than what it must supply needs no exact
 //     value.  A row whose band exceeds kBandCap, or with a non-finite
 //     screened value, takes the exact route: all its exact scores, then the
 //     usual row selector.
@@ -406,10 +405,9 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
 // One wavefront per query block (row), one row per workgroup.  Lane l owns the CL consecutive blocks CL l .. CL l + CL - 1 of
 // the row (keys in registers, sets of them as CL-bit masks), so counts and
 // the ascending output need one prefix sum over lanes, not one per slot.
-// The exact scores of the band come from fp64 tiles laid out as the score
-// kernel lays them out: the A operand holds the 16 rows of the row's 16-row
-// tile (this row at its own position), the B operand holds band blocks; only
-// this row's results are kept.
+// The exact scores of the band come from the score kernel's fp64 sums in
+// their one-row form (score_row16: this row against 16 band blocks per
+// chain); the exact route below still uses whole 16-row tiles.
 template <int D, int CL>
 __global__ __launch_bounds__(64 * kSWaves) void band_select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t rows, int nqb, int nkb,
@@ -501,17 +499,15 @@ __global__ __launch_bounds__(64 * kSWaves) void band_select_kernel(
         for (uint32_t x = band_m; x; x &= x - 1u) s_bandC[w][pos++] = j0 + __builtin_ctz(x);
         s_chosen[w][lane] = 0u;
         __builtin_amdgcn_wave_barrier();
-        // exact scores of the band, 16 blocks per fp64 tile
-        const int i0 = i & ~15, rpos = i - i0;
+        // exact scores of the band, 16 blocks per row chain (lane c < 16: block c0 + c)
         f32x4 qv[D / 16];
-        load_operands<D>(qh + static_cast<int64_t>(min(i0 + lr, nqb - 1)) * D + 4 * lg, qv);
+        load_operands<D>(qh + static_cast<int64_t>(i) * D + 4 * lg, qv);
         for (int c0 = 0; c0 < m; c0 += 16) {
           const int col = s_bandC[w][min(c0 + lr, m - 1)];
           f32x4 kq[D / 16];
           load_operands<D>(kh + static_cast<int64_t>(col) * D + 4 * lg, kq);
-          const f64x4 acc = score_tile16<D>(qv, kq);
-          // fp64 tile layout: lane (lr, lg) holds rows lg + 4 r of column lr
-          if (lg == (rpos & 3) && c0 + lr < m) s_bandF[w][c0 + lr] = static_cast<float>(tau_d * acc[rpos >> 2]);
+          const double acc = score_row16<D>(qv, kq);
+          if (lane < 16 && c0 + lane < m) s_bandF[w][c0 + lane] = static_cast<float>(tau_d * acc);
         }
         __builtin_amdgcn_wave_barrier();
         // keep the best `need` of the band: higher F first, then the lower index
