@@ -405,9 +405,9 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
 // One wavefront per query block (row), one row per workgroup.  Lane l owns the CL consecutive blocks CL l .. CL l + CL - 1 of
 // the row (keys in registers, sets of them as CL-bit masks), so counts and
 // the ascending output need one prefix sum over lanes, not one per slot.
-// The exact scores of the band come from the score kernel's fp64 sums in
-// their one-row form (score_row16: this row against 16 band blocks per
-// chain); the exact route below still uses whole 16-row tiles.
+// The exact scores (of the band, and of every block on the exact route) come
+// from the score kernel's fp64 sums in their one-row form (score_row16: this
+// row against 16 blocks per chain).
 template <int D, int CL>
 __global__ __launch_bounds__(64 * kSWaves) void band_select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t rows, int nqb, int nkb,
@@ -545,16 +545,15 @@ __global__ __launch_bounds__(64 * kSWaves) void band_select_kernel(
   // ---- exact route for this row: every exact score, then the row selector ------
   float* srow = s_exact_rows + w * stride;
   {
-    const int i0 = i & ~15, rpos = i - i0;
     f32x4 qv[D / 16];
-    load_operands<D>(qh + static_cast<int64_t>(min(i0 + lr, nqb - 1)) * D + 4 * lg, qv);
+    load_operands<D>(qh + static_cast<int64_t>(i) * D + 4 * lg, qv);
     const int ntk = (nkb + 15) / 16;
     for (int jt = 0; jt < ntk; ++jt) {
       const int jc = 16 * jt + lr;
       f32x4 kq[D / 16];
       load_operands<D>(kh + static_cast<int64_t>(min(jc, nkb - 1)) * D + 4 * lg, kq);
-      const f64x4 acc = score_tile16<D>(qv, kq);
-      if (lg == (rpos & 3) && jc < nkb) srow[jc] = static_cast<float>(tau_d * acc[rpos >> 2]);
+      const double acc = score_row16<D>(qv, kq);   // lane c < 16: block 16 jt + c
+      if (lane < 16 && jc < nkb) srow[jc] = static_cast<float>(tau_d * acc);
     }
   }
   __builtin_amdgcn_wave_barrier();
