@@ -293,6 +293,7 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
     __syncthreads();                            // the region is the key tile's next
   }
 
+  float ssmax = 0.f;                            // largest squared norm seen (rs == 0)
   // key means split into LDS (bf16 rows, 16-byte chunk ^ (row % 16) for
   // D = 128, ^ ((row / 2) % 8) for D = 64); from the first row strip, the
   // largest squared norm of the strip (rows past nkb repeat the last block)
@@ -314,10 +315,26 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
     *reinterpret_cast<bf16x4*>(s_hi + off) = h;
     *reinterpret_cast<bf16x4*>(s_lo + off) = l;
     if (rs == 0) {
-#pragma unroll
-      for (int d = 1; d < CPB; d <<= 1) ss += __shfl_xor(ss, d);
-      if (ch == 0) atomicMax(s_kmax, __float_as_uint(ss));    // ss >= 0: bits order as values
+      // squared norm of the block: its CPB chunks sit in CPB consecutive
+      // lanes (one or two 16-lane rows); prefix sums within each row, then
+      // row 2r's total added to row 2r + 1, leave it in the block's last lane
+      float v = ss;
+      v += __int_as_float(dpp_i<0x111>(0, __float_as_int(v)));
+      v += __int_as_float(dpp_i<0x112>(0, __float_as_int(v)));
+      v += __int_as_float(dpp_i<0x114>(0, __float_as_int(v)));
+      v += __int_as_float(dpp_i<0x118>(0, __float_as_int(v)));
+      if constexpr (CPB == 32) v += __int_as_float(dpp_i<0x142, 0xa>(0, __float_as_int(v)));
+      ssmax = fmaxf(ssmax, v);
     }
+  }
+  if (rs == 0) {
+    static_assert(CPB == 16 || CPB == 32, "a key-block mean spans one or two 16-lane rows");
+    float m2 = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ssmax), 31)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ssmax), 63)));
+    if constexpr (CPB == 16)
+      m2 = fmaxf(m2, fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ssmax), 15)),
+                           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ssmax), 47))));
+    if (lane == 0) atomicMax(s_kmax, __float_as_uint(m2));   // m2 >= 0: bits order as values
   }
   __syncthreads();
   if (rs == 0 && t == 0) kmaxp[bh * cstrips + cs] = __uint_as_float(*s_kmax);
