@@ -1,6 +1,9 @@
-// One 16 x 16 tile of aggregated block scores on the fp64 matrix cores,
-// shared by the score kernel and the fused score + selection kernel so that
-// both produce bit-identical float32 scores.
+// The exact block scores on the fp64 matrix cores, in the forms the kernels
+// use: a 16 x 16 tile (score_tile16; the score kernel runs two at once,
+// score_tiles16x2) and one row against 16 columns (score_row16, for the band
+// selection's exact scores).  All form the same float64 sums with the same
+// operations in the same order, so every kernel produces the same float32
+// scores bit for bit.
 //
 // v_mfma_f64_16x16x4f64 lane layout (gfx950): A lane l = (row l % 16,
 // k l / 16), B lane l = (k l / 16, column l % 16), result lane l register r =
