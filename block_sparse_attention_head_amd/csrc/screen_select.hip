@@ -426,7 +426,9 @@ __global__ __launch_bounds__(64 * kScrWaves) void screen_kernel(
 // from the score kernel's fp64 sums in their one-row form (score_row16: this
 // row against 16 blocks per chain).
 template <int D, int CL>
-__global__ __launch_bounds__(64 * kSWaves) void band_select_kernel(
+// At most 96 registers (second bound: five waves per SIMD): a row is a
+// latency chain, so more rows in flight shorten the kernel.
+__global__ __launch_bounds__(64 * kSWaves, 5) void band_select_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, int64_t rows, int nqb, int nkb,
     float tau, int nf, int k, const uint16_t* __restrict__ app, const float* __restrict__ kmaxp,
     int cstrips, int ws_stride, int stride, int32_t* __restrict__ cnt, int32_t* __restrict__ idx,
